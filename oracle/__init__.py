@@ -1,0 +1,189 @@
+"""fp64 CPU oracle of the lightning-indexer backward (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never reaches it, and the two share no code.
+
+The arithmetic lives in ``indexer_bwd_oracle.c`` (plain loops in fp64 that
+follow the definition step by step); this module compiles it with gcc and
+marshals numpy arrays.  bf16 inputs are widened to fp64 exactly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "indexer_bwd_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP).  Returns the library path."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O3", "-march=native", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        lp = ctypes.POINTER(ctypes.c_int64)
+        i64 = ctypes.c_int64
+        dbl = ctypes.c_double
+        lib.oracle_sparse.argtypes = [dp, dp, dp, ip, dp, dp] + [i64] * 6 + [dbl, dbl, dp, dp, dp]
+        lib.oracle_sparse_rows.argtypes = [dp, dp, dp, ip, dp, dp] + [i64] * 6 + [dbl, dbl, i64, lp, dp, dp]
+        lib.oracle_sparse_dk_rows.argtypes = [dp, dp, dp, ip, dp, dp] + [i64] * 6 + [dbl, dbl, i64, lp, dp]
+        lib.oracle_dense.argtypes = [dp, dp, dp, dp, dp] + [i64] * 6 + [dbl, dbl, dp, dp, dp]
+        lib.oracle_dense_rows.argtypes = [dp, dp, dp, dp, dp] + [i64] * 6 + [dbl, dbl, i64, lp, dp, dp]
+        lib.oracle_dense_dk_rows.argtypes = [dp, dp, dp, dp, dp] + [i64] * 6 + [dbl, dbl, i64, lp, dp]
+        lib.oracle_score_grad.argtypes = [ctypes.c_int, ip, dp, dp] + [i64] * 5 + [dbl, dbl, dp]
+        for f in ("oracle_sparse", "oracle_sparse_rows", "oracle_sparse_dk_rows", "oracle_dense",
+                  "oracle_dense_rows", "oracle_dense_dk_rows", "oracle_score_grad"):
+            getattr(lib, f).restype = ctypes.c_int
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def _d(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a, ct):
+    return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact fp64 values."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+class Problem:
+    """Inputs of one backward call, held as fp64 (ids int32)."""
+
+    def __init__(self, q, k, w, I, p, ids=None, *, S_k=None, sm_scale=1.0, grad_loss=1.0,
+                 q_offset=0):
+        self.q = _d(q)
+        self.k = _d(k)
+        self.w = _d(w)
+        self.I = _d(I)
+        self.p = _d(p)
+        self.dense = ids is None
+        self.ids = None if ids is None else np.ascontiguousarray(ids, dtype=np.int32)
+        self.B, self.S_q, self.H, self.D = self.q.shape
+        self.S_k = self.k.shape[1] if S_k is None else S_k
+        self.topk = self.S_k if self.dense else self.ids.shape[-1]
+        self.sm_scale = float(sm_scale)
+        self.grad_loss = float(grad_loss)
+        self.q_offset = int(q_offset)
+        assert self.k.shape == (self.B, self.S_k, self.D)
+        assert self.w.shape == (self.B, self.S_q, self.H)
+        assert self.I.shape == (self.B, self.S_q, self.topk) == self.p.shape
+
+    @classmethod
+    def from_inputs(cls, x) -> "Problem":
+        """From a ``synth.Inputs`` (bf16 bits for q/k, fp32 for w/I/p)."""
+        return cls(widen_bf16(x.q), widen_bf16(x.k), x.w, x.index_score, x.attn_score, x.ids,
+                   S_k=x.wl.S_k, sm_scale=x.sm_scale, grad_loss=x.grad_loss,
+                   q_offset=x.wl.q_offset)
+
+    def _head(self):
+        dp = ctypes.c_double
+        return (_ptr(self.q, dp), _ptr(self.k, dp), _ptr(self.w, dp))
+
+    def _shape(self):
+        return (self.B, self.S_q, self.S_k, self.H, self.D)
+
+    def backward(self):
+        """Full backward: (dq [B,S_q,H,D], dw [B,S_q,H], dk [B,S_k,D]) in fp64."""
+        lib = _load()
+        dq = np.zeros((self.B, self.S_q, self.H, self.D))
+        dw = np.zeros((self.B, self.S_q, self.H))
+        dk = np.zeros((self.B, self.S_k, self.D))
+        dp = ctypes.c_double
+        if self.dense:
+            rc = lib.oracle_dense(*self._head(), _ptr(self.I, dp), _ptr(self.p, dp), *self._shape(),
+                                  self.q_offset, self.sm_scale, self.grad_loss, _ptr(dq, dp),
+                                  _ptr(dw, dp), _ptr(dk, dp))
+        else:
+            rc = lib.oracle_sparse(*self._head(), _ptr(self.ids, ctypes.c_int32), _ptr(self.I, dp),
+                                   _ptr(self.p, dp), *self._shape(), self.topk, self.sm_scale,
+                                   self.grad_loss, _ptr(dq, dp), _ptr(dw, dp), _ptr(dk, dp))
+        if rc != 0:
+            raise RuntimeError("oracle failed: %d" % rc)
+        return dq, dw, dk
+
+    def rows(self, rows: Sequence[int]):
+        """dQ, dW of the listed rows (flat b*S_q + t): ([n,H,D], [n,H])."""
+        lib = _load()
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        dq = np.zeros((len(r), self.H, self.D))
+        dw = np.zeros((len(r), self.H))
+        dp = ctypes.c_double
+        lp = ctypes.c_int64
+        if self.dense:
+            rc = lib.oracle_dense_rows(*self._head(), _ptr(self.I, dp), _ptr(self.p, dp),
+                                       *self._shape(), self.q_offset, self.sm_scale, self.grad_loss,
+                                       len(r), _ptr(r, lp), _ptr(dq, dp), _ptr(dw, dp))
+        else:
+            rc = lib.oracle_sparse_rows(*self._head(), _ptr(self.ids, ctypes.c_int32),
+                                        _ptr(self.I, dp), _ptr(self.p, dp), *self._shape(), self.topk,
+                                        self.sm_scale, self.grad_loss, len(r), _ptr(r, lp),
+                                        _ptr(dq, dp), _ptr(dw, dp))
+        if rc != 0:
+            raise RuntimeError("oracle failed: %d" % rc)
+        return dq, dw
+
+    def dk_rows(self, keys: Sequence[int]):
+        """dK of the listed key rows (flat b*S_k + s): [n,D]."""
+        lib = _load()
+        kk = np.ascontiguousarray(keys, dtype=np.int64)
+        dk = np.zeros((len(kk), self.D))
+        dp = ctypes.c_double
+        lp = ctypes.c_int64
+        if self.dense:
+            rc = lib.oracle_dense_dk_rows(*self._head(), _ptr(self.I, dp), _ptr(self.p, dp),
+                                          *self._shape(), self.q_offset, self.sm_scale,
+                                          self.grad_loss, len(kk), _ptr(kk, lp), _ptr(dk, dp))
+        else:
+            rc = lib.oracle_sparse_dk_rows(*self._head(), _ptr(self.ids, ctypes.c_int32),
+                                           _ptr(self.I, dp), _ptr(self.p, dp), *self._shape(),
+                                           self.topk, self.sm_scale, self.grad_loss, len(kk),
+                                           _ptr(kk, lp), _ptr(dk, dp))
+        if rc != 0:
+            raise RuntimeError("oracle failed: %d" % rc)
+        return dk
+
+    def score_grad(self):
+        """dI of every row: [B,S_q,topk] (dense: [B,S_q,S_k])."""
+        lib = _load()
+        dI = np.zeros(self.I.shape)
+        dp = ctypes.c_double
+        ids = self.ids if self.ids is not None else np.zeros(1, np.int32)
+        rc = lib.oracle_score_grad(int(self.dense), _ptr(ids, ctypes.c_int32), _ptr(self.I, dp),
+                                   _ptr(self.p, dp), self.B, self.S_q, self.S_k, self.topk,
+                                   self.q_offset, self.sm_scale, self.grad_loss, _ptr(dI, dp))
+        if rc != 0:
+            raise RuntimeError("oracle failed: %d" % rc)
+        return dI
+
