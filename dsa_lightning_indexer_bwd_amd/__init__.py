@@ -1,0 +1,191 @@
+"""Python binding of the MI355X lightning-indexer backward (C ABI via ctypes).
+
+The functions here only marshal arguments: they check tensor dtypes, devices
+and contiguity, allocate outputs when the caller passes none, and call the
+entry points of ``libdsa_indexer_bwd.so`` with raw device pointers and the
+current HIP stream.  Every step of the backward runs in the HIP kernels; there
+is no fallback.  If the library is not built this module raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "indexer_bwd_sparse",
+    "indexer_bwd_dense",
+    "indexer_bwd_workspace_bytes",
+    "indexer_bwd_strerror",
+    "library",
+    "IBWD_OK",
+    "IBWD_ERR_INVALID_ARGUMENT",
+    "IBWD_ERR_UNSUPPORTED_DEVICE",
+    "IBWD_ERR_HIP",
+    "IBWD_FLAG_DETERMINISTIC",
+    "IndexerBwdError",
+]
+
+IBWD_OK = 0
+IBWD_ERR_INVALID_ARGUMENT = -1
+IBWD_ERR_UNSUPPORTED_DEVICE = -2
+IBWD_ERR_HIP = -3
+IBWD_FLAG_DETERMINISTIC = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_indexer_bwd.so")
+_lib = None
+
+
+class IndexerBwdError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__("indexer_bwd failed (%d): %s" % (status, indexer_bwd_strerror(status)))
+
+
+def library() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("HIP library %s is missing: run __graft_entry__.build() first" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        f32 = ctypes.c_float
+        lib.indexer_bwd_sparse.argtypes = [vp] * 9 + [i64] * 6 + [f32, f32, ctypes.c_uint32, vp,
+                                                                  ctypes.c_size_t, vp]
+        lib.indexer_bwd_sparse.restype = ctypes.c_int
+        lib.indexer_bwd_dense.argtypes = [vp] * 8 + [i64] * 6 + [f32, f32, ctypes.c_uint32, vp,
+                                                                 ctypes.c_size_t, vp]
+        lib.indexer_bwd_dense.restype = ctypes.c_int
+        lib.indexer_bwd_workspace_bytes.argtypes = [ctypes.c_int] + [i64] * 6 + [ctypes.c_uint32]
+        lib.indexer_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.indexer_bwd_strerror.argtypes = [ctypes.c_int]
+        lib.indexer_bwd_strerror.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def indexer_bwd_strerror(status: int) -> str:
+    return library().indexer_bwd_strerror(int(status)).decode()
+
+
+def indexer_bwd_workspace_bytes(dense: bool, B: int, S_q: int, S_k: int, H: int, D: int, topk: int,
+                                flags: int = 0) -> int:
+    return int(library().indexer_bwd_workspace_bytes(int(bool(dense)), B, S_q, S_k, H, D, topk,
+                                                     flags))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, dtype, shape, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_cuda:
+        raise ValueError("%s must live on the GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream_handle(stream, device) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _outputs(q, k, d_q, d_w, d_k):
+    torch = _torch()
+    B, S_q, H, D = q.shape
+    S_k = k.shape[1]
+    if d_q is None:
+        d_q = torch.empty((B, S_q, H, D), dtype=torch.float32, device=q.device)
+    if d_w is None:
+        d_w = torch.empty((B, S_q, H), dtype=torch.float32, device=q.device)
+    if d_k is None:
+        d_k = torch.empty((B, S_k, D), dtype=torch.float32, device=q.device)
+    return d_q, d_w, d_k
+
+
+def _workspace(dense, B, S_q, S_k, H, D, topk, flags, workspace, device):
+    torch = _torch()
+    need = indexer_bwd_workspace_bytes(dense, B, S_q, S_k, H, D, topk, flags)
+    if need == 0:
+        return workspace, 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w=None, d_k=None, *,
+                       sm_scale: float = 1.0, grad_loss: float = 1.0, deterministic: bool = False,
+                       workspace=None, stream=None) -> Tuple:
+    """Backward of the top-k indexer.  Returns (d_q, d_w, d_k), all fp32.
+
+    q [B,S_q,H,D] bf16, k [B,S_k,D] bf16, w [B,S_q,H] fp32, topk_ids [B,S_q,topk]
+    int32, index_score / attn_score [B,S_q,topk] fp32.  Outputs are overwritten.
+    """
+    torch = _torch()
+    B, S_q, H, D = q.shape
+    S_k = k.shape[1]
+    topk = topk_ids.shape[-1]
+    _check(q, torch.bfloat16, (B, S_q, H, D), "q")
+    _check(k, torch.bfloat16, (B, S_k, D), "k")
+    _check(w, torch.float32, (B, S_q, H), "w")
+    _check(topk_ids, torch.int32, (B, S_q, topk), "topk_ids")
+    _check(index_score, torch.float32, (B, S_q, topk), "index_score")
+    _check(attn_score, torch.float32, (B, S_q, topk), "attn_score")
+    d_q, d_w, d_k = _outputs(q, k, d_q, d_w, d_k)
+    _check(d_q, torch.float32, (B, S_q, H, D), "d_q")
+    _check(d_w, torch.float32, (B, S_q, H), "d_w")
+    _check(d_k, torch.float32, (B, S_k, D), "d_k")
+    flags = IBWD_FLAG_DETERMINISTIC if deterministic else 0
+    workspace, ws_bytes = _workspace(False, B, S_q, S_k, H, D, topk, flags, workspace, q.device)
+    st = library().indexer_bwd_sparse(
+        _ptr(q), _ptr(k), _ptr(w), _ptr(topk_ids), _ptr(index_score), _ptr(attn_score), _ptr(d_q),
+        _ptr(d_w), _ptr(d_k), B, S_q, S_k, H, D, topk, float(sm_scale), float(grad_loss), flags,
+        _ptr(workspace), ws_bytes, _stream_handle(stream, q.device))
+    if st != IBWD_OK:
+        raise IndexerBwdError(st)
+    return d_q, d_w, d_k
+
+
+def indexer_bwd_dense(q, k, w, index_score, attn_score, d_q=None, d_w=None, d_k=None, *,
+                      q_offset: int = 0, sm_scale: float = 1.0, grad_loss: float = 1.0,
+                      deterministic: bool = False, workspace=None, stream=None) -> Tuple:
+    """Backward of the dense causal indexer (key s selected iff s <= t + q_offset).
+
+    index_score / attn_score are [B,S_q,S_k] fp32.  Returns (d_q, d_w, d_k).
+    """
+    torch = _torch()
+    B, S_q, H, D = q.shape
+    S_k = k.shape[1]
+    _check(q, torch.bfloat16, (B, S_q, H, D), "q")
+    _check(k, torch.bfloat16, (B, S_k, D), "k")
+    _check(w, torch.float32, (B, S_q, H), "w")
+    _check(index_score, torch.float32, (B, S_q, S_k), "index_score")
+    _check(attn_score, torch.float32, (B, S_q, S_k), "attn_score")
+    d_q, d_w, d_k = _outputs(q, k, d_q, d_w, d_k)
+    _check(d_q, torch.float32, (B, S_q, H, D), "d_q")
+    _check(d_w, torch.float32, (B, S_q, H), "d_w")
+    _check(d_k, torch.float32, (B, S_k, D), "d_k")
+    flags = IBWD_FLAG_DETERMINISTIC if deterministic else 0
+    workspace, ws_bytes = _workspace(True, B, S_q, S_k, H, D, S_k, flags, workspace, q.device)
+    st = library().indexer_bwd_dense(
+        _ptr(q), _ptr(k), _ptr(w), _ptr(index_score), _ptr(attn_score), _ptr(d_q), _ptr(d_w),
+        _ptr(d_k), B, S_q, S_k, H, D, int(q_offset), float(sm_scale), float(grad_loss), flags,
+        _ptr(workspace), ws_bytes, _stream_handle(stream, q.device))
+    if st != IBWD_OK:
+        raise IndexerBwdError(st)
+    return d_q, d_w, d_k

@@ -1,0 +1,59 @@
+"""Ahead-of-time build of the HIP library (hipcc, gfx950), in-tree."""
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libdsa_indexer_bwd.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+
+HIP_SOURCES = ["indexer_bwd_kernels.hip"]
+HOST_SOURCES = ["indexer_bwd_api.cpp"]
+
+# Device code: gfx950 only; packed-fp32 VALU forms disabled (they are formed
+# by the compiler from ordinary float code otherwise).
+DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build(verbose: bool = False) -> str:
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS
+        _run(cmd, verbose)
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
+        _run(cmd, verbose)
+        objs.append(obj)
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    _run([hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs, verbose)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in res.stdout.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if res.returncode != 0:
+        raise RuntimeError("build failed: %s\n%s" % (" ".join(cmd), out))
+    if verbose and out.strip():
+        print(out)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,175 @@
+// C ABI of the lightning-indexer backward: argument validation, the device
+// check, and the launch sequence.  Every check runs before the first write or
+// launch, so an invalid call leaves the outputs untouched.
+#include "dsa_indexer_bwd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];
+
+int device_status() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return IBWD_ERR_HIP;
+  if (dev >= kMaxDevices) return IBWD_ERR_UNSUPPORTED_DEVICE;
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    g_dev_ok[dev] = 0;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      g_dev_ok[dev] = -1;
+      return;
+    }
+    g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  });
+  if (g_dev_ok[dev] < 0) return IBWD_ERR_HIP;
+  return g_dev_ok[dev] ? IBWD_OK : IBWD_ERR_UNSUPPORTED_DEVICE;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+
+bool fits(int64_t a, int64_t b) { return a > 0 && b > 0 && a <= kMaxElems / b; }
+bool fits(int64_t a, int64_t b, int64_t c) { return fits(a, b) && fits(a * b, c); }
+bool fits(int64_t a, int64_t b, int64_t c, int64_t d) { return fits(a, b, c) && fits(a * b * c, d); }
+
+// Shape and pointer checks common to both entry points.
+int check_common(const void* q, const void* k, const float* w, const float* I, const float* p,
+                 float* d_q, float* d_w, float* d_k, int64_t B, int64_t S_q, int64_t S_k,
+                 int64_t H, int64_t D, int64_t row_len, uint32_t flags) {
+  if (!q || !k || !w || !I || !p || !d_q || !d_w || !d_k) return IBWD_ERR_INVALID_ARGUMENT;
+  if (B < 1 || S_q < 1 || S_k < 1 || H < 1 || D < 1 || row_len < 1) return IBWD_ERR_INVALID_ARGUMENT;
+  if (H > ibwd::kMaxHeads) return IBWD_ERR_INVALID_ARGUMENT;
+  if (D != 32 && D != 64 && D != 128) return IBWD_ERR_INVALID_ARGUMENT;
+  if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, row_len))
+    return IBWD_ERR_INVALID_ARGUMENT;
+  if ((flags & ~IBWD_FLAG_DETERMINISTIC) != 0) return IBWD_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(d_q, 16) || !aligned(d_k, 16))
+    return IBWD_ERR_INVALID_ARGUMENT;
+  if (!aligned(w, 4) || !aligned(I, 4) || !aligned(p, 4) || !aligned(d_w, 4))
+    return IBWD_ERR_INVALID_ARGUMENT;
+  return IBWD_OK;
+}
+
+size_t workspace_bytes(int64_t B, int64_t S_k, int64_t D, uint32_t flags) {
+  if (!(flags & IBWD_FLAG_DETERMINISTIC)) return 0;
+  return ibwd::det_workspace_bytes(B, S_k, D);
+}
+
+}  // namespace
+
+extern "C" {
+
+int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32_t* topk_ids,
+                       const float* index_score, const float* attn_score, float* d_q, float* d_w,
+                       float* d_k, int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
+                       int64_t topk, float sm_scale, float grad_loss, uint32_t flags,
+                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(q, k, w, index_score, attn_score, d_q, d_w, d_k, B, S_q, S_k, H, D, topk,
+                        flags);
+  if (st != IBWD_OK) return st;
+  if (!topk_ids || !aligned(topk_ids, 4)) return IBWD_ERR_INVALID_ARGUMENT;
+  size_t need = workspace_bytes(B, S_k, D, flags);
+  if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256)))
+    return IBWD_ERR_INVALID_ARGUMENT;
+  st = device_status();
+  if (st != IBWD_OK) return st;
+  ibwd::Problem P{};
+  P.q = static_cast<const uint16_t*>(q);
+  P.k = static_cast<const uint16_t*>(k);
+  P.w = w;
+  P.ids = topk_ids;
+  P.I = index_score;
+  P.p = attn_score;
+  P.dq = d_q;
+  P.dw = d_w;
+  P.dk = d_k;
+  P.B = B;
+  P.S_q = S_q;
+  P.S_k = S_k;
+  P.H = H;
+  P.D = D;
+  P.row_len = topk;
+  P.dense = false;
+  P.q_offset = 0;
+  P.sm_scale = sm_scale;
+  P.grad_loss = grad_loss;
+  P.deterministic = (flags & IBWD_FLAG_DETERMINISTIC) != 0;
+  P.workspace = workspace;
+  return ibwd::launch(P, stream) == hipSuccess ? IBWD_OK : IBWD_ERR_HIP;
+}
+
+int indexer_bwd_dense(const void* q, const void* k, const float* w, const float* index_score,
+                      const float* attn_score, float* d_q, float* d_w, float* d_k, int64_t B,
+                      int64_t S_q, int64_t S_k, int64_t H, int64_t D, int64_t q_offset,
+                      float sm_scale, float grad_loss, uint32_t flags, void* workspace,
+                      size_t ws_bytes, hipStream_t stream) {
+  int st = check_common(q, k, w, index_score, attn_score, d_q, d_w, d_k, B, S_q, S_k, H, D, S_k,
+                        flags);
+  if (st != IBWD_OK) return st;
+  if (q_offset < -(int64_t(1) << 40) || q_offset > (int64_t(1) << 40))
+    return IBWD_ERR_INVALID_ARGUMENT;
+  size_t need = workspace_bytes(B, S_k, D, flags);
+  if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256)))
+    return IBWD_ERR_INVALID_ARGUMENT;
+  st = device_status();
+  if (st != IBWD_OK) return st;
+  ibwd::Problem P{};
+  P.q = static_cast<const uint16_t*>(q);
+  P.k = static_cast<const uint16_t*>(k);
+  P.w = w;
+  P.ids = nullptr;
+  P.I = index_score;
+  P.p = attn_score;
+  P.dq = d_q;
+  P.dw = d_w;
+  P.dk = d_k;
+  P.B = B;
+  P.S_q = S_q;
+  P.S_k = S_k;
+  P.H = H;
+  P.D = D;
+  P.row_len = S_k;
+  P.dense = true;
+  P.q_offset = q_offset;
+  P.sm_scale = sm_scale;
+  P.grad_loss = grad_loss;
+  P.deterministic = (flags & IBWD_FLAG_DETERMINISTIC) != 0;
+  P.workspace = workspace;
+  return ibwd::launch(P, stream) == hipSuccess ? IBWD_OK : IBWD_ERR_HIP;
+}
+
+size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_k, int64_t H,
+                                   int64_t D, int64_t topk, uint32_t flags) {
+  (void)S_q;
+  (void)H;
+  if (B < 1 || S_k < 1 || D < 1 || (!dense && topk < 1)) return 0;
+  if (!fits(B, S_k, D)) return 0;
+  return workspace_bytes(B, S_k, D, flags);
+}
+
+const char* indexer_bwd_strerror(int status) {
+  switch (status) {
+    case IBWD_OK:
+      return "ok";
+    case IBWD_ERR_INVALID_ARGUMENT:
+      return "invalid argument (null pointer, unsupported shape, misaligned pointer, bad flags "
+             "or workspace too small)";
+    case IBWD_ERR_UNSUPPORTED_DEVICE:
+      return "unsupported device (gfx950 / MI355X required)";
+    case IBWD_ERR_HIP:
+      return "HIP runtime or launch error";
+    default:
+      return "unknown status";
+  }
+}
+
+}  // extern "C"

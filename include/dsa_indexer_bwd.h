@@ -1,0 +1,128 @@
+/*
+ * dsa_indexer_bwd.h — C ABI of the MI355X (gfx950) backward pass of the
+ * DeepSeek-Sparse-Attention lightning indexer.
+ *
+ * The indexer scores query t against key s as
+ *     I[t,s] = sum_h w[t,h] * relu(q[t,h,:] . k[s,:])
+ * restricted to per-query top-k key ids.  The backward pass defined by the
+ * fp64 reference of NVIDIA/cudnn-frontend PR #730 (its posted A/B benchmark
+ * harness, `ref_grads`, together with the kernel-1 score-gradient contract in
+ * the same harness docstring) is, per query row t with valid slot set
+ * V = { j : 0 <= id_j < S_k }:
+ *     dI_j      = grad_loss * sm_scale * (softmax_V(sm_scale * I[t,:])_j - p[t,j])
+ *     S[h,j]    = q[t,h,:] . k[id_j,:]
+ *     G[h,j]    = dI_j * w[t,h] * [S[h,j] > 0]
+ *     d_w[t,h]  = sum_{j in V} dI_j * max(S[h,j], 0)
+ *     d_q[t,h,:]= sum_{j in V} G[h,j] * k[id_j,:]
+ *     d_k[s,:]  = sum over every (t, j in V) with id_j = s of sum_h G[h,j] * q[t,h,:]
+ * (index_score is I, attn_score is the target distribution p.)
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major, contiguous, and live in device memory
+ *     of the current HIP device.  bf16 tensors are passed as their 16-bit
+ *     patterns (`const void*`).
+ *   - Shapes: q [B,S_q,H,D] bf16, k [B,S_k,D] bf16, w [B,S_q,H] fp32,
+ *     d_q [B,S_q,H,D] fp32, d_w [B,S_q,H] fp32, d_k [B,S_k,D] fp32.
+ *   - Ids are local to each batch: 0 <= id < S_k selects key id of the same
+ *     batch; every other value (-1 canonically, any negative, any >= S_k) is a
+ *     padding slot that contributes nothing, whatever index_score/attn_score
+ *     hold there (PR #730 review thread: a positive out-of-range local id is
+ *     padding and must not alias the next batch; harness padding battery).
+ *     Duplicate ids are independent slots.
+ *   - Ownership: the caller owns every buffer.  The library allocates nothing,
+ *     frees nothing, keeps no state between calls apart from a per-device cache
+ *     of the device check, never synchronises, and only enqueues work on
+ *     `stream` (0 = the null stream).  Inputs are read-only (attn_score too).
+ *     d_q, d_w and d_k are overwritten in full (d_k is zeroed by the library).
+ *   - Alignment: q, k, d_q, d_k must be 16-byte aligned; w, index_score,
+ *     attn_score, topk_ids, d_w 4-byte aligned.
+ *   - Supported shapes: 1 <= H <= 64, D in {32, 64, 128}; every dimension >= 1;
+ *     element counts below 2^31 per tensor.
+ *   - Errors: every argument is validated before anything is written or
+ *     launched, so on error the outputs are untouched.  Launch failures are
+ *     reported by the HIP error of the launch; execution errors surface on the
+ *     stream as usual for HIP.
+ *   - Determinism: d_q and d_w are bitwise reproducible run to run.  d_k is
+ *     accumulated with fp32 atomics and may differ in the last bits between
+ *     runs (PR #549: dK uses fp32 atomicAdd and is run-to-run nondeterministic)
+ *     unless IBWD_FLAG_DETERMINISTIC is set.
+ */
+#ifndef DSA_INDEXER_BWD_H
+#define DSA_INDEXER_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define IBWD_OK 0
+#define IBWD_ERR_INVALID_ARGUMENT -1 /* null pointer, bad shape, misaligned, workspace too small */
+#define IBWD_ERR_UNSUPPORTED_DEVICE -2 /* the current device is not gfx950 */
+#define IBWD_ERR_HIP -3              /* a HIP runtime call or launch failed */
+
+/* Flags. */
+#define IBWD_FLAG_DETERMINISTIC 1u /* bitwise run-to-run d_k: fixed-point integer accumulation
+                                      in the caller's workspace, then conversion to fp32 */
+
+/*
+ * indexer_bwd_sparse — backward of the top-k (sparse) indexer.
+ *
+ *   topk_ids     [B,S_q,topk] int32, batch-local key ids (see padding above)
+ *   index_score  [B,S_q,topk] fp32, the forward scores I of the selected slots
+ *   attn_score   [B,S_q,topk] fp32, the target distribution p over the valid
+ *                slots (read-only; the kernel never writes it)
+ *   sm_scale     scale applied to I inside the softmax and as chain factor
+ *   grad_loss    upstream gradient of the KL loss (a scalar)
+ *   flags        0 or IBWD_FLAG_DETERMINISTIC
+ *   workspace    device scratch of at least indexer_bwd_workspace_bytes(...)
+ *                bytes (may be NULL when that size is 0); 256-byte aligned
+ *   stream       HIP stream the work is enqueued on
+ *
+ * Returns IBWD_OK or one of the IBWD_ERR_* codes.
+ */
+int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32_t* topk_ids,
+                       const float* index_score, const float* attn_score, float* d_q, float* d_w,
+                       float* d_k, int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
+                       int64_t topk, float sm_scale, float grad_loss, uint32_t flags,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * indexer_bwd_dense — backward of the dense causal indexer: query t of a batch
+ * selects every key s with 0 <= s <= t + q_offset (and s < S_k); a row with no
+ * such key contributes nothing (PR #549 names a separate dense indexer-backward
+ * test; PR #730 keeps the q-causal-offset behaviour).
+ *
+ *   index_score  [B,S_q,S_k] fp32, I[t,s]; entries with s > t + q_offset are ignored
+ *   attn_score   [B,S_q,S_k] fp32, p[t,s]; same masking
+ *   q_offset     causal offset (may be negative)
+ *
+ * Other arguments as for indexer_bwd_sparse.
+ */
+int indexer_bwd_dense(const void* q, const void* k, const float* w, const float* index_score,
+                      const float* attn_score, float* d_q, float* d_w, float* d_k, int64_t B,
+                      int64_t S_q, int64_t S_k, int64_t H, int64_t D, int64_t q_offset,
+                      float sm_scale, float grad_loss, uint32_t flags, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * indexer_bwd_workspace_bytes — device scratch needed by a call with these
+ * arguments (dense != 0 selects indexer_bwd_dense; topk is ignored then).
+ * 0 when no workspace is needed.  Returns 0 for invalid shapes as well; the
+ * call itself reports those.
+ */
+size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_k, int64_t H,
+                                   int64_t D, int64_t topk, uint32_t flags);
+
+/* indexer_bwd_strerror — static text for a status code (never NULL). */
+const char* indexer_bwd_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_INDEXER_BWD_H */
