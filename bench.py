@@ -21,7 +21,7 @@ sys.path.insert(0, ROOT)
 METRIC = "indexer-bwd µs + TFLOP/s (frac of MFMA peak) at S_q=8192,S_k=4096,topk=1024"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-COMPUTE_DTYPE = "f32"       # row-wise kernel: fp32 FMA on bf16 inputs
+COMPUTE_DTYPE = "bf16"      # MFMA operands bf16, fp32 accumulation and outputs
 
 
 def parse():

@@ -283,16 +283,13 @@ hipError_t launch(const Problem& P, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     det_bound_kernel<<<dim3(unsigned(rows)), kThreads, 0, stream>>>(P);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    rowwise_bwd_kernel<true>
-        <<<dim3(unsigned(rows)), kThreads, rowwise_smem_bytes(P), stream>>>(P);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch_mfma(P, stream)) != hipSuccess) return err;
     det_finalize_kernel<<<fill_blocks, 256, 0, stream>>>(P, dk_elems);
     return hipGetLastError();
   }
   zero_u32_kernel<<<fill_blocks, 256, 0, stream>>>(reinterpret_cast<uint32_t*>(P.dk), dk_elems);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  rowwise_bwd_kernel<false><<<dim3(unsigned(rows)), kThreads, rowwise_smem_bytes(P), stream>>>(P);
-  return hipGetLastError();
+  return launch_mfma(P, stream);
 }
 
 }  // namespace ibwd

@@ -40,4 +40,8 @@ inline size_t det_workspace_bytes(int64_t B, int64_t S_k, int64_t D) {
 // Enqueue the whole backward on `stream`.  Returns the first HIP error.
 hipError_t launch(const Problem& P, hipStream_t stream);
 
+// The MFMA main kernel (one wave per query row); d_k must already be zeroed
+// (or the deterministic workspace prepared).
+hipError_t launch_mfma(const Problem& P, hipStream_t stream);
+
 }  // namespace ibwd
