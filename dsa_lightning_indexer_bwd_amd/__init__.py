@@ -23,6 +23,7 @@ __all__ = [
     "IBWD_ERR_UNSUPPORTED_DEVICE",
     "IBWD_ERR_HIP",
     "IBWD_FLAG_DETERMINISTIC",
+    "IBWD_FLAG_ATOMIC_DK",
     "IndexerBwdError",
 ]
 
@@ -31,6 +32,7 @@ IBWD_ERR_INVALID_ARGUMENT = -1
 IBWD_ERR_UNSUPPORTED_DEVICE = -2
 IBWD_ERR_HIP = -3
 IBWD_FLAG_DETERMINISTIC = 1
+IBWD_FLAG_ATOMIC_DK = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_indexer_bwd.so")
 _lib = None
@@ -128,13 +130,18 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
+def _flags(deterministic: bool, atomic_dk: bool) -> int:
+    return (IBWD_FLAG_DETERMINISTIC if deterministic else 0) | (IBWD_FLAG_ATOMIC_DK if atomic_dk else 0)
+
+
 def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w=None, d_k=None, *,
                        sm_scale: float = 1.0, grad_loss: float = 1.0, deterministic: bool = False,
-                       workspace=None, stream=None) -> Tuple:
+                       atomic_dk: bool = False, workspace=None, stream=None) -> Tuple:
     """Backward of the top-k indexer.  Returns (d_q, d_w, d_k), all fp32.
 
     q [B,S_q,H,D] bf16, k [B,S_k,D] bf16, w [B,S_q,H] fp32, topk_ids [B,S_q,topk]
     int32, index_score / attn_score [B,S_q,topk] fp32.  Outputs are overwritten.
+    atomic_dk selects the single-pass fp32-atomic dK route (no workspace).
     """
     torch = _torch()
     B, S_q, H, D = q.shape
@@ -150,7 +157,7 @@ def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w
     _check(d_q, torch.float32, (B, S_q, H, D), "d_q")
     _check(d_w, torch.float32, (B, S_q, H), "d_w")
     _check(d_k, torch.float32, (B, S_k, D), "d_k")
-    flags = IBWD_FLAG_DETERMINISTIC if deterministic else 0
+    flags = _flags(deterministic, atomic_dk)
     workspace, ws_bytes = _workspace(False, B, S_q, S_k, H, D, topk, flags, workspace, q.device)
     st = library().indexer_bwd_sparse(
         _ptr(q), _ptr(k), _ptr(w), _ptr(topk_ids), _ptr(index_score), _ptr(attn_score), _ptr(d_q),
@@ -163,7 +170,8 @@ def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w
 
 def indexer_bwd_dense(q, k, w, index_score, attn_score, d_q=None, d_w=None, d_k=None, *,
                       q_offset: int = 0, sm_scale: float = 1.0, grad_loss: float = 1.0,
-                      deterministic: bool = False, workspace=None, stream=None) -> Tuple:
+                      deterministic: bool = False, atomic_dk: bool = False, workspace=None,
+                      stream=None) -> Tuple:
     """Backward of the dense causal indexer (key s selected iff s <= t + q_offset).
 
     index_score / attn_score are [B,S_q,S_k] fp32.  Returns (d_q, d_w, d_k).
@@ -180,7 +188,7 @@ def indexer_bwd_dense(q, k, w, index_score, attn_score, d_q=None, d_w=None, d_k=
     _check(d_q, torch.float32, (B, S_q, H, D), "d_q")
     _check(d_w, torch.float32, (B, S_q, H), "d_w")
     _check(d_k, torch.float32, (B, S_k, D), "d_k")
-    flags = IBWD_FLAG_DETERMINISTIC if deterministic else 0
+    flags = _flags(deterministic, atomic_dk)
     workspace, ws_bytes = _workspace(True, B, S_q, S_k, H, D, S_k, flags, workspace, q.device)
     st = library().indexer_bwd_dense(
         _ptr(q), _ptr(k), _ptr(w), _ptr(index_score), _ptr(attn_score), _ptr(d_q), _ptr(d_w),

@@ -1,0 +1,102 @@
+// Device helpers shared by the gfx950 kernels: MFMA wrappers, bf16 packing,
+// LDS transpose reads and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace ibwd {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_32x32x16_bf16.  Lane layouts (checked on the device):
+//   A[m][k]: lane l holds m = l%32, k = 8*(l/32) + e   (e = 0..7)
+//   B[k][n]: lane l holds n = l%32, k = 8*(l/32) + e
+//   D[m][n]: lane l holds n = l%32, m = 8*i + 4*(l/32) + r in register 4*i + r
+__device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_bf16.  Lane layouts (checked on the device):
+//   A[m][k]: lane l holds m = l%16, k = 8*(l/16) + e
+//   B[k][n]: lane l holds n = l%16, k = 8*(l/16) + e
+//   D[m][n]: lane l holds n = l%16, m = 4*(l/16) + r in register r
+__device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// ds_read_b64_tr_b16 (gfx950 LDS transpose read).  Within each 16-lane group,
+// source lane s reads 4 consecutive bf16 at its own address; the result of lane
+// i, element e is source lane (4e + i/4)'s element (i%4) (measured on the
+// device).  With source lane s pointing at row (row0 + s/4), columns
+// col0 + 4*(s%4) .. +3 of a row-major bf16 tile, lane i receives column
+// col0 + i of rows row0 .. row0+3: a 4 x 16 block read transposed.
+__device__ __forceinline__ uint2 lds_tr4(const unsigned char* tile, int pitch, int row0, int col0) {
+  const int s = threadIdx.x & 15;
+  const unsigned char* a = tile + (row0 + (s >> 2)) * pitch + (col0 + 4 * (s & 3)) * 2;
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(a));
+  return __builtin_bit_cast(uint2, v);
+}
+// An MFMA operand of 8 k-values: rows [r0, r0+4) then [r1, r1+4) of a tile,
+// at column col0 + (lane % 16).
+__device__ __forceinline__ u32x4_t lds_tr8(const unsigned char* tile, int pitch, int r0, int r1,
+                                           int col0) {
+  const uint2 x = lds_tr4(tile, pitch, r0, col0);
+  const uint2 y = lds_tr4(tile, pitch, r1, col0);
+  return u32x4_t{x.x, x.y, y.x, y.y};
+}
+
+// Keep the compiler from moving LDS accesses across this point.  One wave's
+// LDS operations execute in issue order, so this is all that lanes exchanging
+// data through LDS inside one wave need.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// v_writelane_b32 through the compiler intrinsic, so that the backend knows
+// the instruction and inserts the wait states it needs after the VALU write of
+// the scalar source (a hand-written asm statement gets none).
+extern "C" __device__ int __ibwd_writelane_i32(int val, int lane, int old) __asm(
+    "llvm.amdgcn.writelane.i32");
+// Lane `lane` of the result takes the wave-uniform `val`.
+__device__ __forceinline__ uint32_t write_lane(uint32_t old, uint32_t val, int lane) {
+  return uint32_t(__ibwd_writelane_i32(int(val), lane, int(old)));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = threadIdx.x & 63;
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+}  // namespace ibwd

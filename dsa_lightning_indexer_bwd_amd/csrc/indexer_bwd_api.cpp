@@ -51,7 +51,11 @@ int check_common(const void* q, const void* k, const float* w, const float* I, c
   if (D != 32 && D != 64 && D != 128) return IBWD_ERR_INVALID_ARGUMENT;
   if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, row_len))
     return IBWD_ERR_INVALID_ARGUMENT;
-  if ((flags & ~IBWD_FLAG_DETERMINISTIC) != 0) return IBWD_ERR_INVALID_ARGUMENT;
+  if ((flags & ~(IBWD_FLAG_DETERMINISTIC | IBWD_FLAG_ATOMIC_DK)) != 0) return IBWD_ERR_INVALID_ARGUMENT;
+  if ((flags & IBWD_FLAG_DETERMINISTIC) && (flags & IBWD_FLAG_ATOMIC_DK)) return IBWD_ERR_INVALID_ARGUMENT;
+  // the row kernel buckets a row's slots into at most kMaxRanges key ranges
+  if ((S_k + ibwd::kRangeKeys - 1) / ibwd::kRangeKeys > ibwd::kMaxRanges)
+    return IBWD_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(d_q, 16) || !aligned(d_k, 16))
     return IBWD_ERR_INVALID_ARGUMENT;
   if (!aligned(w, 4) || !aligned(I, 4) || !aligned(p, 4) || !aligned(d_w, 4))
@@ -59,9 +63,10 @@ int check_common(const void* q, const void* k, const float* w, const float* I, c
   return IBWD_OK;
 }
 
-size_t workspace_bytes(int64_t B, int64_t S_k, int64_t D, uint32_t flags) {
-  if (!(flags & IBWD_FLAG_DETERMINISTIC)) return 0;
-  return ibwd::det_workspace_bytes(B, S_k, D);
+size_t workspace_bytes(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
+                       int64_t row_len, uint32_t flags) {
+  if (flags & IBWD_FLAG_ATOMIC_DK) return 0;
+  return ibwd::make_layout(B, S_q, S_k, H, D, row_len).total;
 }
 
 }  // namespace
@@ -77,7 +82,7 @@ int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32
                         flags);
   if (st != IBWD_OK) return st;
   if (!topk_ids || !aligned(topk_ids, 4)) return IBWD_ERR_INVALID_ARGUMENT;
-  size_t need = workspace_bytes(B, S_k, D, flags);
+  size_t need = workspace_bytes(B, S_q, S_k, H, D, topk, flags);
   if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256)))
     return IBWD_ERR_INVALID_ARGUMENT;
   st = device_status();
@@ -102,9 +107,8 @@ int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32
   P.q_offset = 0;
   P.sm_scale = sm_scale;
   P.grad_loss = grad_loss;
-  P.deterministic = (flags & IBWD_FLAG_DETERMINISTIC) != 0;
-  P.workspace = workspace;
-  return ibwd::launch(P, stream) == hipSuccess ? IBWD_OK : IBWD_ERR_HIP;
+  P.route = (flags & IBWD_FLAG_ATOMIC_DK) ? ibwd::kDkAtomic : ibwd::kDkTwoPass;
+  return ibwd::launch(P, workspace, stream) == hipSuccess ? IBWD_OK : IBWD_ERR_HIP;
 }
 
 int indexer_bwd_dense(const void* q, const void* k, const float* w, const float* index_score,
@@ -117,7 +121,7 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
   if (st != IBWD_OK) return st;
   if (q_offset < -(int64_t(1) << 40) || q_offset > (int64_t(1) << 40))
     return IBWD_ERR_INVALID_ARGUMENT;
-  size_t need = workspace_bytes(B, S_k, D, flags);
+  size_t need = workspace_bytes(B, S_q, S_k, H, D, S_k, flags);
   if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256)))
     return IBWD_ERR_INVALID_ARGUMENT;
   st = device_status();
@@ -142,18 +146,17 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
   P.q_offset = q_offset;
   P.sm_scale = sm_scale;
   P.grad_loss = grad_loss;
-  P.deterministic = (flags & IBWD_FLAG_DETERMINISTIC) != 0;
-  P.workspace = workspace;
-  return ibwd::launch(P, stream) == hipSuccess ? IBWD_OK : IBWD_ERR_HIP;
+  P.route = (flags & IBWD_FLAG_ATOMIC_DK) ? ibwd::kDkAtomic : ibwd::kDkTwoPass;
+  return ibwd::launch(P, workspace, stream) == hipSuccess ? IBWD_OK : IBWD_ERR_HIP;
 }
 
 size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_k, int64_t H,
                                    int64_t D, int64_t topk, uint32_t flags) {
-  (void)S_q;
-  (void)H;
-  if (B < 1 || S_k < 1 || D < 1 || (!dense && topk < 1)) return 0;
-  if (!fits(B, S_k, D)) return 0;
-  return workspace_bytes(B, S_k, D, flags);
+  const int64_t row_len = dense ? S_k : topk;
+  if (B < 1 || S_q < 1 || S_k < 1 || H < 1 || H > ibwd::kMaxHeads || row_len < 1) return 0;
+  if (D != 32 && D != 64 && D != 128) return 0;
+  if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, row_len)) return 0;
+  return workspace_bytes(B, S_q, S_k, H, D, row_len, flags);
 }
 
 const char* indexer_bwd_strerror(int status) {

@@ -9,6 +9,61 @@
 namespace ibwd {
 
 constexpr int64_t kMaxHeads = 64;
+constexpr int kSlots = 32;          // slots per chunk in the row kernel
+constexpr int kRangeKeys = 256;     // keys per range of the two-pass dK route
+constexpr int kMaxRanges = 1024;    // ranges a row can be bucketed into (S_k <= 262144)
+constexpr int kMaxQueryBlock = 1024;  // queries per range-kernel workgroup
+
+enum DkRoute : int {
+  kDkTwoPass = 0,  // masks + records exported, range-major LDS reduction (deterministic)
+  kDkAtomic = 1,   // fp32 global atomics straight from the row kernel
+};
+
+// Workspace layout of the two-pass dK route.
+//   rec   [rows][row_len + 32] int4 {key, dI bits, sign bits of h 0..31,
+//         sign bits of h 32..63}: the valid slots of a row grouped by key range
+//         (range r = key / RK), slot order within a range; the last 32 entries
+//         of a row take the row kernel's stores of padding lanes
+//   off   [rows][NR+1]    int: start of each range's records within the row
+//   qt    [rows][D][HP]   bf16: (w*q)^T of every row, heads padded to HP
+//   slab  [B][NQB][NR*RK][D] fp32: per query block partial dK
+struct Layout {
+  int64_t rows, row_len, rec_stride, HP, RK, NR, NQB, QBS, nchunk;
+  size_t off_rec, off_off, off_qt, off_slab, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
+                          int64_t row_len) {
+  Layout L{};
+  L.rows = B * S_q;
+  L.row_len = row_len;
+  L.rec_stride = row_len + kSlots;
+  L.HP = H > 32 ? 64 : 32;
+  L.RK = kRangeKeys;
+  L.NR = (S_k + L.RK - 1) / L.RK;
+  // about 256 range-kernel workgroups (one per CU), at most kMaxQueryBlock
+  // queries each
+  int64_t nqb = (256 + L.NR * B - 1) / (L.NR * B);
+  if (nqb < (S_q + kMaxQueryBlock - 1) / kMaxQueryBlock) nqb = (S_q + kMaxQueryBlock - 1) / kMaxQueryBlock;
+  if (nqb > S_q) nqb = S_q;
+  if (nqb < 1) nqb = 1;
+  L.QBS = (S_q + nqb - 1) / nqb;
+  L.NQB = (S_q + L.QBS - 1) / L.QBS;
+  L.nchunk = (row_len + kSlots - 1) / kSlots;
+  size_t o = 0;
+  L.off_rec = o;
+  o = align256(o + size_t(L.rows) * size_t(L.rec_stride) * 16);
+  L.off_off = o;
+  o = align256(o + size_t(L.rows) * size_t(L.NR + 1) * 4);
+  L.off_qt = o;
+  o = align256(o + size_t(L.rows) * size_t(D) * size_t(L.HP) * 2);
+  L.off_slab = o;
+  o = align256(o + size_t(B) * size_t(L.NQB) * size_t(L.NR * L.RK) * size_t(D) * 4);
+  L.total = o;
+  return L;
+}
 
 // One validated backward call.  Pointers are device pointers; shapes follow
 // the public header.  For the dense variant ids == nullptr and row_len == S_k.
@@ -26,22 +81,23 @@ struct Problem {
   bool dense;
   int64_t q_offset;
   float sm_scale, grad_loss;
-  bool deterministic;
-  void* workspace;
+  int route;            // DkRoute
+  // two-pass exports (carved from the workspace)
+  int4* rec;
+  int* off;
+  uint16_t* qt;
+  float* slab;
+  int64_t rec_stride, RK, NR, NQB, QBS, nchunk, HP;
 };
 
-// Workspace of the deterministic route: a 256-byte header (the magnitude
-// bound) followed by one int64 fixed-point accumulator per d_k element.
-constexpr size_t kDetHeaderBytes = 256;
-inline size_t det_workspace_bytes(int64_t B, int64_t S_k, int64_t D) {
-  return kDetHeaderBytes + size_t(B) * size_t(S_k) * size_t(D) * sizeof(int64_t);
-}
-
 // Enqueue the whole backward on `stream`.  Returns the first HIP error.
-hipError_t launch(const Problem& P, hipStream_t stream);
+hipError_t launch(Problem P, void* workspace, hipStream_t stream);
 
-// The MFMA main kernel (one wave per query row); d_k must already be zeroed
-// (or the deterministic workspace prepared).
-hipError_t launch_mfma(const Problem& P, hipStream_t stream);
+// Row kernel (one wave per query row): dQ, dW and either the dK atomics or the
+// two-pass exports.
+hipError_t launch_rows(const Problem& P, hipStream_t stream);
+// Two-pass dK: range-major reduction into per query-block slabs, then the
+// fixed-order sum of the slabs into d_k.
+hipError_t launch_dk(const Problem& P, hipStream_t stream);
 
 }  // namespace ibwd

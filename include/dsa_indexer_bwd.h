@@ -37,15 +37,20 @@
  *   - Alignment: q, k, d_q, d_k must be 16-byte aligned; w, index_score,
  *     attn_score, topk_ids, d_w 4-byte aligned.
  *   - Supported shapes: 1 <= H <= 64, D in {32, 64, 128}; every dimension >= 1;
- *     element counts below 2^31 per tensor.
+ *     element counts below 2^31 per tensor; S_k <= 262144.
  *   - Errors: every argument is validated before anything is written or
  *     launched, so on error the outputs are untouched.  Launch failures are
  *     reported by the HIP error of the launch; execution errors surface on the
  *     stream as usual for HIP.
- *   - Determinism: d_q and d_w are bitwise reproducible run to run.  d_k is
- *     accumulated with fp32 atomics and may differ in the last bits between
- *     runs (PR #549: dK uses fp32 atomicAdd and is run-to-run nondeterministic)
- *     unless IBWD_FLAG_DETERMINISTIC is set.
+ *   - dK routes.  The default route reduces the dK scatter in two passes: the
+ *     row kernel exports each slot's sign mask [S > 0] and dI into the caller's
+ *     workspace, and a range-major kernel rebuilds and sums the contributions
+ *     in on-chip memory, then the per query-block partial sums are added in a
+ *     fixed order.  d_q, d_w and d_k are all bitwise reproducible run to run.
+ *     IBWD_FLAG_ATOMIC_DK selects the single-pass route of the pages' design
+ *     instead: fp32 global atomics straight from the row kernel, no workspace,
+ *     and d_k may then differ in the last bits between runs (PR #549: dK uses
+ *     fp32 atomicAdd and is run-to-run nondeterministic).
  */
 #ifndef DSA_INDEXER_BWD_H
 #define DSA_INDEXER_BWD_H
@@ -66,8 +71,10 @@ extern "C" {
 #define IBWD_ERR_HIP -3              /* a HIP runtime call or launch failed */
 
 /* Flags. */
-#define IBWD_FLAG_DETERMINISTIC 1u /* bitwise run-to-run d_k: fixed-point integer accumulation
-                                      in the caller's workspace, then conversion to fp32 */
+#define IBWD_FLAG_DETERMINISTIC 1u /* request the bitwise-reproducible route (the default
+                                      two-pass route; conflicts with IBWD_FLAG_ATOMIC_DK) */
+#define IBWD_FLAG_ATOMIC_DK 2u     /* single-pass dK with fp32 global atomics; no workspace;
+                                      d_k not bitwise reproducible */
 
 /*
  * indexer_bwd_sparse — backward of the top-k (sparse) indexer.
@@ -78,7 +85,7 @@ extern "C" {
  *                slots (read-only; the kernel never writes it)
  *   sm_scale     scale applied to I inside the softmax and as chain factor
  *   grad_loss    upstream gradient of the KL loss (a scalar)
- *   flags        0 or IBWD_FLAG_DETERMINISTIC
+ *   flags        0, IBWD_FLAG_DETERMINISTIC or IBWD_FLAG_ATOMIC_DK
  *   workspace    device scratch of at least indexer_bwd_workspace_bytes(...)
  *                bytes (may be NULL when that size is 0); 256-byte aligned
  *   stream       HIP stream the work is enqueued on
@@ -112,8 +119,11 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
 /*
  * indexer_bwd_workspace_bytes — device scratch needed by a call with these
  * arguments (dense != 0 selects indexer_bwd_dense; topk is ignored then).
- * 0 when no workspace is needed.  Returns 0 for invalid shapes as well; the
- * call itself reports those.
+ * The default route needs 16 bytes per slot (plus 512 per row), (w*q)^T in
+ * bf16 (2*H_pad*D bytes per row, H_pad = 32 or 64) and the per query-block dK
+ * partial sums (about 320 MB in all at B=1, S_q=8192, S_k=4096, H=64, D=128,
+ * topk=1024); IBWD_FLAG_ATOMIC_DK needs none (0).
+ * Returns 0 for invalid shapes as well; the call itself reports those.
  */
 size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_k, int64_t H,
                                    int64_t D, int64_t topk, uint32_t flags);

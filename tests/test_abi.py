@@ -30,11 +30,16 @@ def test_library_exports_every_declared_symbol():
 def test_strerror_and_workspace():
     for st in (0, -1, -2, -3, 7):
         assert isinstance(ibwd.indexer_bwd_strerror(st), str)
-    assert ibwd.indexer_bwd_workspace_bytes(False, 1, 8192, 4096, 64, 128, 1024, 0) == 0
-    det = ibwd.indexer_bwd_workspace_bytes(False, 1, 8192, 4096, 64, 128, 1024, 1)
-    assert det >= 4096 * 128 * 8
-    assert ibwd.indexer_bwd_workspace_bytes(True, 2, 64, 64, 4, 32, 0, 1) >= 2 * 64 * 32 * 8
-    assert ibwd.indexer_bwd_workspace_bytes(False, 0, 1, 1, 1, 32, 1, 1) == 0
+    # default (two-pass) route: 16-byte slot records, (w*q)^T in bf16, dK partial slabs
+    ws = ibwd.indexer_bwd_workspace_bytes(False, 1, 8192, 4096, 64, 128, 1024, 0)
+    assert ws >= 8192 * 1024 * 16 + 8192 * 64 * 128 * 2 + 4096 * 128 * 4
+    assert ws == ibwd.indexer_bwd_workspace_bytes(False, 1, 8192, 4096, 64, 128, 1024,
+                                                  ibwd.IBWD_FLAG_DETERMINISTIC)
+    assert ibwd.indexer_bwd_workspace_bytes(False, 1, 8192, 4096, 64, 128, 1024,
+                                            ibwd.IBWD_FLAG_ATOMIC_DK) == 0
+    assert ibwd.indexer_bwd_workspace_bytes(True, 2, 64, 64, 4, 32, 0, 0) >= 2 * 64 * 64 * 16
+    assert ibwd.indexer_bwd_workspace_bytes(False, 0, 1, 1, 1, 32, 1, 0) == 0
+    assert ibwd.indexer_bwd_workspace_bytes(False, 1, 1, 1, 1, 48, 1, 0) == 0
 
 
 # fake, 256-byte aligned "device" addresses: every case below must be rejected
@@ -45,7 +50,7 @@ A = 0x10000000
 def sparse_args(**kw):
     a = dict(q=A, k=A + 0x100000, w=A + 0x200000, ids=A + 0x300000, I=A + 0x400000, p=A + 0x500000,
              dq=A + 0x600000, dw=A + 0x700000, dk=A + 0x800000, B=1, S_q=64, S_k=128, H=4, D=32,
-             topk=16, sm=1.0, gl=1.0, flags=0, ws=None, ws_bytes=0, stream=None)
+             topk=16, sm=1.0, gl=1.0, flags=0, ws=A + 0x1000000, ws_bytes=1 << 30, stream=None)
     a.update(kw)
     return a
 
@@ -61,10 +66,10 @@ def call_sparse(a):
     dict(q=None), dict(k=None), dict(w=None), dict(ids=None), dict(I=None), dict(p=None),
     dict(dq=None), dict(dw=None), dict(dk=None),
     dict(B=0), dict(S_q=0), dict(S_k=-1), dict(H=0), dict(H=65), dict(D=48), dict(D=256),
-    dict(topk=0), dict(flags=2), dict(q=A + 8), dict(dk=A + 0x800004), dict(w=A + 0x200002),
-    dict(flags=1, ws=None, ws_bytes=0), dict(flags=1, ws=A + 0x900000, ws_bytes=16),
-    dict(flags=1, ws=A + 0x900010, ws_bytes=1 << 30),
-    dict(B=1 << 20, S_q=1 << 20, H=64, D=128),
+    dict(topk=0), dict(flags=3), dict(flags=4), dict(q=A + 8), dict(dk=A + 0x800004),
+    dict(w=A + 0x200002), dict(ws=None, ws_bytes=0), dict(ws=A + 0x900000, ws_bytes=16),
+    dict(ws=A + 0x900010, ws_bytes=1 << 30), dict(flags=1, ws=None, ws_bytes=1 << 30),
+    dict(B=1 << 20, S_q=1 << 20, H=64, D=128), dict(S_k=1024 * 256 + 1, D=128, ws_bytes=1 << 40),
 ])
 def test_sparse_rejects_invalid_arguments(bad):
     assert call_sparse(sparse_args(**bad)) == ibwd.IBWD_ERR_INVALID_ARGUMENT
@@ -74,8 +79,11 @@ def test_dense_rejects_invalid_arguments():
     lib = ibwd.library()
     base = [A, A + 0x100000, A + 0x200000, A + 0x400000, A + 0x500000, A + 0x600000, A + 0x700000,
             A + 0x800000]
-    assert lib.indexer_bwd_dense(*base[:3], None, *base[4:], 1, 16, 16, 4, 32, 0, 1.0, 1.0, 0, None,
+    assert lib.indexer_bwd_dense(*base[:3], None, *base[4:], 1, 16, 16, 4, 32, 0, 1.0, 1.0, 2, None,
                                  0, None) == ibwd.IBWD_ERR_INVALID_ARGUMENT
+    # default route without workspace
+    assert lib.indexer_bwd_dense(*base, 1, 16, 16, 4, 32, 0, 1.0, 1.0, 0, None, 0,
+                                 None) == ibwd.IBWD_ERR_INVALID_ARGUMENT
     assert lib.indexer_bwd_dense(*base, 1, 16, 16, 4, 40, 0, 1.0, 1.0, 0, None, 0,
                                  None) == ibwd.IBWD_ERR_INVALID_ARGUMENT
     assert lib.indexer_bwd_dense(*base, 1, 16, 0, 4, 32, 0, 1.0, 1.0, 0, None, 0,
@@ -88,5 +96,5 @@ def test_valid_arguments_without_gpu_fail_cleanly():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: covered by the GPU tests")
-    st = call_sparse(sparse_args())
-    assert st in (ibwd.IBWD_ERR_HIP, ibwd.IBWD_ERR_UNSUPPORTED_DEVICE)
+    for a in (sparse_args(), sparse_args(flags=ibwd.IBWD_FLAG_ATOMIC_DK, ws=None, ws_bytes=0)):
+        assert call_sparse(a) in (ibwd.IBWD_ERR_HIP, ibwd.IBWD_ERR_UNSUPPORTED_DEVICE)

@@ -49,16 +49,16 @@ def dev_inputs(x):
     return out
 
 
-def run(ibwd, x, t=None, deterministic=False):
+def run(ibwd, x, t=None, deterministic=False, atomic_dk=False):
     t = dev_inputs(x) if t is None else t
     if x.ids is None:
         r = ibwd.indexer_bwd_dense(t["q"], t["k"], t["w"], t["I"], t["p"], q_offset=x.wl.q_offset,
                                    sm_scale=x.sm_scale, grad_loss=x.grad_loss,
-                                   deterministic=deterministic)
+                                   deterministic=deterministic, atomic_dk=atomic_dk)
     else:
         r = ibwd.indexer_bwd_sparse(t["q"], t["k"], t["w"], t["ids"], t["I"], t["p"],
                                     sm_scale=x.sm_scale, grad_loss=x.grad_loss,
-                                    deterministic=deterministic)
+                                    deterministic=deterministic, atomic_dk=atomic_dk)
     torch.cuda.synchronize()
     return [a.cpu().numpy() for a in r]
 
@@ -165,32 +165,48 @@ def test_padding_equivalence(ibwd):
     assert relrms(alt[2], base[2]) < 1e-6
 
 
-def test_run_to_run(ibwd):
-    log("case: run-to-run determinism")
+def test_run_to_run_bitwise(ibwd):
+    """The default route is bitwise reproducible for all three outputs."""
+    log("case: run-to-run determinism (default route)")
     x = make_inputs("anchor", S_q=256, seed=13)
     t = dev_inputs(x)
     a = run(ibwd, x, t)
-    b = run(ibwd, x, t)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
-    assert relrms(a[2], b[2]) < 1e-5
-
-
-def test_deterministic_flag(ibwd):
-    log("case: deterministic route")
-    x = make_inputs("anchor", S_q=128, seed=17)
-    t = dev_inputs(x)
-    a = run(ibwd, x, t, deterministic=True)
     b = run(ibwd, x, t, deterministic=True)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
-    assert_parity("deterministic", a, oracle.Problem.from_inputs(x).backward())
-    xd = make_inputs(dataclasses.replace(WORKLOADS["dense"], S_q=64, S_k=64), seed=4)
-    td = dev_inputs(xd)
-    a = run(ibwd, xd, td, deterministic=True)
-    b = run(ibwd, xd, td, deterministic=True)
-    for u, v in zip(a, b):
-        assert np.array_equal(u, v)
-    assert_parity("deterministic-dense", a, oracle.Problem.from_inputs(xd).backward())
+
+
+@pytest.mark.parametrize("name", ["tiny", "anchor", "dense"])
+def test_atomic_route(ibwd, name):
+    """The single-pass fp32-atomic dK route: parity, and d_q/d_w bitwise run to run."""
+    log(f"case: atomic route {name}")
+    x = make_inputs(name, S_q=min(WORKLOADS[name].S_q, 96), seed=23)
+    t = dev_inputs(x)
+    a = run(ibwd, x, t, atomic_dk=True)
+    b = run(ibwd, x, t, atomic_dk=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert relrms(a[2], b[2]) < 1e-5
+    assert_parity(f"atomic-{name}", a, oracle.Problem.from_inputs(x).backward())
+    d = run(ibwd, x, t)
+    assert np.array_equal(a[0], d[0]) and np.array_equal(a[1], d[1])
+
+
+@pytest.mark.parametrize("atomic_dk", [False, True])
+def test_duplicate_ids(ibwd, atomic_dk):
+    """Duplicate ids in a row are independent slots (both routes; the default
+    route's range kernel takes its ordered path for tiles with repeated keys)."""
+    log(f"case: duplicate ids atomic={atomic_dk}")
+    wl = dataclasses.replace(WORKLOADS["anchor"], S_q=48, S_k=300, topk=200, pad_frac=0.05)
+    x = make_inputs(wl, seed=31)
+    rng = np.random.default_rng(5)
+    # every row: a third of its slots repeat keys of the row (some several times)
+    for t in range(wl.S_q):
+        src = rng.integers(0, wl.topk, size=wl.topk // 3)
+        dst = rng.integers(0, wl.topk, size=wl.topk // 3)
+        x.ids[0, t, dst] = x.ids[0, t, src]
+    x.ids[0, 0, :] = 7          # a row of one key repeated
+    got = run(ibwd, x, atomic_dk=atomic_dk)
+    assert_parity(f"dup-atomic{int(atomic_dk)}", got, oracle.Problem.from_inputs(x).backward())
 
 
 def test_inputs_are_not_modified(ibwd):
