@@ -174,93 +174,110 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 1) void dk_range_kernel(Proble
     return P.rec[int64_t(row) * P.rec_stride + i];
   };
 
-  if (nne > 0) {
-    u32x4_t qa[S::MT][NH];
-    int4 e = list[0];
-    load_qt(e.x, qa);
-    bool vcur;
-    int4 rcur = load_rec(e.x, e.y + l16, e.z, vcur);
-    for (int qi = 0; qi < nne; ++qi) {
-      e = list[qi];
-      const int4 en = list[qi + 1 < nne ? qi + 1 : qi];
-      u32x4_t qn[S::MT][NH];
-      load_qt(en.x, qn);
-      const int ntl = (e.z - e.y + kTile - 1) / kTile;
-      for (int tt = 0; tt < ntl; ++tt) {
-        // prefetch the next tile's record (next query's first tile at the end)
-        const bool same_q = tt + 1 < ntl;
-        const int nrow = same_q ? e.x : en.x;
-        const int nidx = same_q ? e.y + kTile * (tt + 1) + l16 : en.y + l16;
-        const int nend = same_q ? e.z : (qi + 1 < nne ? en.z : 0);
-        bool vnext;
-        const int4 rnext = load_rec(nrow, nidx, nend, vnext);
-
-        // ---- the current tile ----------------------------------------------
-        const int key = rcur.x;
-        const float dI = __int_as_float(rcur.y);
-        const bool vm = vcur;
-        u32x4_t bop[NH];
+  // one 16-slot tile: the lane's record r (slot l16), valid flag vm, A operand qa
+  auto process = [&](const int4& r, bool vm, const u32x4_t (&qa)[S::MT][NH]) {
+    const int key = r.x;
+    const float dI = __int_as_float(r.y);
+    u32x4_t bop[NH];
 #pragma unroll
-        for (int ks = 0; ks < NH; ++ks) {
-          const uint32_t word = vm ? uint32_t(ks == 0 ? rcur.z : rcur.w) : 0u;
-          bop[ks] = lut[(word >> (8 * grp)) & 0xffu];
+    for (int ks = 0; ks < NH; ++ks) {
+      const uint32_t word = vm ? uint32_t(ks == 0 ? r.z : r.w) : 0u;
+      bop[ks] = lut[(word >> (8 * grp)) & 0xffu];
+    }
+    // are the tile's keys pairwise distinct?
+    if (lane < kTile && vm) stamp[key - R0] = lane;
+    wave_lds_sync();
+    const bool clash = lane < kTile && vm && stamp[key - R0] != lane;
+    const bool distinct = ballot(clash) == 0;
+
+    f32x4_t acc[S::MT];
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NH; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt) acc[mt] = mfma16(qa[mt][ks], bop[ks], acc[mt]);
+
+    // lane holds slot l16, d = d0 + 16*mt + 4*grp + (0..3)
+    float* rowp = slab + (key - R0) * S::kPitch + d0 + 4 * grp;
+    if (distinct) {
+      if (vm) {
+        float4 old[S::MT];
+#pragma unroll
+        for (int mt = 0; mt < S::MT; ++mt) old[mt] = *reinterpret_cast<const float4*>(rowp + 16 * mt);
+#pragma unroll
+        for (int mt = 0; mt < S::MT; ++mt) {
+          float4 v = old[mt];
+          v.x = fmaf(dI, acc[mt][0], v.x);
+          v.y = fmaf(dI, acc[mt][1], v.y);
+          v.z = fmaf(dI, acc[mt][2], v.z);
+          v.w = fmaf(dI, acc[mt][3], v.w);
+          *reinterpret_cast<float4*>(rowp + 16 * mt) = v;
         }
-        // are the tile's keys pairwise distinct?
-        if (lane < kTile && vm) stamp[key - R0] = lane;
-        wave_lds_sync();
-        const bool clash = lane < kTile && vm && stamp[key - R0] != lane;
-        const bool distinct = ballot(clash) == 0;
-
-        f32x4_t acc[S::MT];
-#pragma unroll
-        for (int mt = 0; mt < S::MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NH; ++ks)
-#pragma unroll
-          for (int mt = 0; mt < S::MT; ++mt) acc[mt] = mfma16(qa[mt][ks], bop[ks], acc[mt]);
-
-        // lane holds slot l16, d = d0 + 16*mt + 4*grp + (0..3)
-        float* rowp = slab + (key - R0) * S::kPitch + d0 + 4 * grp;
-        if (distinct) {
-          if (vm) {
-            float4 old[S::MT];
-#pragma unroll
-            for (int mt = 0; mt < S::MT; ++mt) old[mt] = *reinterpret_cast<const float4*>(rowp + 16 * mt);
-#pragma unroll
-            for (int mt = 0; mt < S::MT; ++mt) {
-              float4 v = old[mt];
-              v.x = fmaf(dI, acc[mt][0], v.x);
-              v.y = fmaf(dI, acc[mt][1], v.y);
-              v.z = fmaf(dI, acc[mt][2], v.z);
-              v.w = fmaf(dI, acc[mt][3], v.w);
-              *reinterpret_cast<float4*>(rowp + 16 * mt) = v;
-            }
-          }
-        } else {
-          // ordered path: one slot of the tile at a time
-          for (int m = 0; m < kTile; ++m) {
-            if (l16 == m && vm) {
-#pragma unroll
-              for (int mt = 0; mt < S::MT; ++mt) {
-                float4 v = *reinterpret_cast<const float4*>(rowp + 16 * mt);
-                v.x = fmaf(dI, acc[mt][0], v.x);
-                v.y = fmaf(dI, acc[mt][1], v.y);
-                v.z = fmaf(dI, acc[mt][2], v.z);
-                v.w = fmaf(dI, acc[mt][3], v.w);
-                *reinterpret_cast<float4*>(rowp + 16 * mt) = v;
-              }
-            }
-            wave_lds_sync();
-          }
-        }
-        wave_lds_sync();
-        rcur = rnext;
-        vcur = vnext;
       }
+    } else {
+      // ordered path: one slot of the tile at a time
+      for (int m = 0; m < kTile; ++m) {
+        if (l16 == m && vm) {
 #pragma unroll
-      for (int mt = 0; mt < S::MT; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < NH; ++ks) qa[mt][ks] = qn[mt][ks];
+          for (int mt = 0; mt < S::MT; ++mt) {
+            float4 v = *reinterpret_cast<const float4*>(rowp + 16 * mt);
+            v.x = fmaf(dI, acc[mt][0], v.x);
+            v.y = fmaf(dI, acc[mt][1], v.y);
+            v.z = fmaf(dI, acc[mt][2], v.z);
+            v.w = fmaf(dI, acc[mt][3], v.w);
+            *reinterpret_cast<float4*>(rowp + 16 * mt) = v;
+          }
+        }
+        wave_lds_sync();
+      }
+    }
+    wave_lds_sync();
+  };
+  // all tiles of one query; f/fv is the record of its first tile, loaded a
+  // query earlier.  Records are prefetched one tile ahead with the loop
+  // unrolled by two so that no loaded register is copied (a copy would wait
+  // for the load).
+  auto run_query = [&](const int4& e, const u32x4_t (&qa)[S::MT][NH], const int4& f, bool fv) {
+    const int ntl = (e.z - e.y + kTile - 1) / kTile;
+    bool vb;
+    int4 rb = load_rec(e.x, e.y + kTile + l16, e.z, vb);
+    process(f, fv, qa);
+    for (int tt = 1; tt < ntl; tt += 2) {
+      bool va;
+      const int4 ra = load_rec(e.x, e.y + kTile * (tt + 1) + l16, e.z, va);
+      process(rb, vb, qa);
+      rb = load_rec(e.x, e.y + kTile * (tt + 2) + l16, e.z, vb);
+      if (tt + 1 < ntl) process(ra, va, qa);
+    }
+  };
+
+  if (nne > 0) {
+    // queries alternate between two operand sets, each loaded one query ahead
+    u32x4_t qa0[S::MT][NH], qa1[S::MT][NH];
+    int4 f0, f1;
+    bool fv0, fv1;
+    {
+      const int4 e0 = list[0];
+      const int4 e1 = list[nne > 1 ? 1 : 0];
+      load_qt(e0.x, qa0);
+      f0 = load_rec(e0.x, e0.y + l16, e0.z, fv0);
+      load_qt(e1.x, qa1);
+      f1 = load_rec(e1.x, e1.y + l16, nne > 1 ? e1.z : 0, fv1);
+    }
+    for (int qi = 0; qi < nne; qi += 2) {
+      run_query(list[qi], qa0, f0, fv0);
+      {
+        const int4 e2 = list[qi + 2 < nne ? qi + 2 : nne - 1];
+        load_qt(e2.x, qa0);
+        f0 = load_rec(e2.x, e2.y + l16, qi + 2 < nne ? e2.z : 0, fv0);
+      }
+      if (qi + 1 < nne) run_query(list[qi + 1], qa1, f1, fv1);
+      {
+        const int4 e3 = list[qi + 3 < nne ? qi + 3 : nne - 1];
+        load_qt(e3.x, qa1);
+        f1 = load_rec(e3.x, e3.y + l16, qi + 3 < nne ? e3.z : 0, fv1);
+      }
     }
   }
   __syncthreads();

@@ -317,11 +317,18 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
   int4* recrow = (ROUTE == kDkTwoPass) ? P.rec + r * P.rec_stride : nullptr;
   float* dkb = (ROUTE == kDkAtomic) ? P.dk + b * P.S_k * D : nullptr;
 
+  // The record of chunk c is stored at the top of iteration c+1, right after
+  // the one wait of the iteration: gfx9's vmcnt also counts stores, and a store
+  // in flight makes the next wait on a load a full drain, so every global
+  // access is issued early and waited for only at the end of the iteration.
+  int prev_pos = row_len + l32;  // the first store goes to the row's tail
+  int4 prev_rec = make_int4(-1, 0, 0, 0);
   for (int c = 0; c < nchunks; ++c) {
     // slot data of chunk c+1 (loaded one chunk ago) -> stage ring; its K rows
     // and the slot data of chunk c+2 go in flight
     float dIn;
     const int key_n = finalize(c + 1, raw_next, dIn);
+    if (ROUTE == kDkTwoPass) recrow[prev_pos] = prev_rec;
     u32x4_t knext[KD];
     gather(key_n, knext);
     raw_next = load_raw(c + 2);
@@ -424,8 +431,8 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
         if (valid && (same & lanemask_lt()) == 0) cursor[rg] = base + __popcll(same);
       }
       // padding lanes and the upper half-wave store into the row's tail
-      if (!valid) pos = row_len + l32;
-      recrow[pos] = make_int4(key, __float_as_int(sd[l32]), int(m0), int(m1));
+      prev_pos = valid ? pos : row_len + l32;
+      prev_rec = make_int4(key, __float_as_int(sd[l32]), int(m0), int(m1));
     } else {
       wave_lds_sync();  // G' tile complete
       // ---- GEMM3: C[j][d] = G'^T[j][h] Q'[h][d], then the dK scatter ----------
@@ -468,6 +475,8 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
     store_k(c + 1, knext, key_n);
     wave_lds_sync();
   }
+
+  if (ROUTE == kDkTwoPass) recrow[prev_pos] = prev_rec;
 
   // ---- row epilogue: dQ = w * dQ', dW -----------------------------------------
   float* dqrow = P.dq + r * P.H * D;
