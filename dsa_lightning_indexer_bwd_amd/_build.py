@@ -9,7 +9,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libdsa_indexer_bwd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-HIP_SOURCES = ["indexer_bwd_kernels.hip", "indexer_bwd_rows.hip", "indexer_bwd_dk.hip"]
+HIP_SOURCES = ["indexer_bwd_kernels.hip", "indexer_bwd_rows.hip", "indexer_bwd_rows_export.hip",
+               "indexer_bwd_dk.hip"]
 HOST_SOURCES = ["indexer_bwd_api.cpp"]
 
 # Device code: gfx950 only; packed-fp32 VALU forms disabled (they are formed

@@ -13,18 +13,21 @@
 // [S > 0] over h}, grouped by key range, plus (w*q)^T per row; this kernel
 // rebuilds C with bf16 MFMA and reduces it with plain LDS read-modify-write:
 //
-//   workgroup (key range R of 256 keys, query block, batch): an fp32 slab
-//   [256][D] in LDS.  Each wave owns D/NW columns, so no two waves ever touch
-//   the same LDS word; all waves walk the same stream of 16-slot tiles:
-//     C^T tile [16 d x 16 slots] = (w*q)^T[16 d x HP] . M[HP x 16 slots]
-//   on v_mfma 16x16x32, with M[h][slot] = [S > 0] in bf16 (0 or 1) looked up
-//   per byte of the sign bits in a 256-entry table, and dI scaling the slot in
-//   fp32.  A lane then holds 4 consecutive d of one slot and adds them into the
-//   slab row of the slot's key with one 16-byte read and one 16-byte write.
-//   Within a tile the 16 keys are distinct unless a row repeats an id; such a
-//   tile takes an ordered one-slot-at-a-time path, so duplicates stay exact.
-//   The next tile's records and the next query's (w*q)^T are loaded while the
-//   current tile computes.
+//   workgroup (key range of 256 keys, query block, batch): an fp32 slab
+//   [256 + 1][D] in LDS (the extra row absorbs the writes of empty tile rows).
+//   Wave w owns the columns 32w .. 32w+31, so no two waves touch the same LDS
+//   word; all waves walk the same stream of 32-slot tiles:
+//     C tile [32 slots x 32 d] = M[32 slots x HP] . (w*q)^T[HP x 32 d]
+//   on v_mfma 32x32x16, with M[slot][h] = [S > 0] in bf16 (0 or 1.0) expanded
+//   from the sign words by two VALU operations per pair of heads, and dI
+//   scaling each slot in fp32.  In the accumulator layout a half-wave holds 32
+//   consecutive columns of one slot, so every LDS read-modify-write touches
+//   32 consecutive words of one slab row per half-wave: with a row pitch of D
+//   words no two lanes of a half-wave share a bank, whatever the keys.
+//   A tile's 32 keys are distinct unless a row repeats an id; a tile with a
+//   repeated key takes an ordered one-row-at-a-time path, so duplicates stay
+//   exact.  The next tile's records and the next query's (w*q)^T are loaded
+//   while the current tile computes.
 // The slab of every (range, query block) goes to global memory, and a last
 // kernel sums the query-block slabs in a fixed order: the result does not
 // depend on scheduling, so d_k is bitwise reproducible.
@@ -38,21 +41,18 @@
 namespace ibwd {
 namespace {
 
-constexpr int kTile = 16;  // slots per MFMA tile (N of 16x16x32)
+constexpr int kTile = 32;  // slots per MFMA tile (M of 32x32x16)
+constexpr int kXcds = 8;   // accelerator dies of the chip, each with its own L2
 
 template <int D>
 struct DkShape {
-  static constexpr int NW = D >= 64 ? 4 : 2;  // waves; each owns DW columns
-  static constexpr int DW = D / NW;
-  static constexpr int MT = DW / 16;          // 16-row m tiles of d per wave
+  static constexpr int NW = D >= 32 ? D / 32 : 1;  // waves; wave w owns columns 32w..32w+31
   static constexpr int RK = kRangeKeys;
-  static constexpr int kPitch = D + 4;        // floats per slab row (bank spread)
-  static constexpr int kSlabBytes = RK * kPitch * 4;
-  static constexpr int kLutOff = kSlabBytes;
-  static constexpr int kStampOff = kLutOff + 256 * 16;
+  static constexpr int kSlabBytes = (RK + 1) * D * 4;  // row RK: sink of empty tile rows
+  static constexpr int kStampOff = kSlabBytes;
   static constexpr int kListOff = kStampOff + NW * RK * 4;
   static constexpr int kBytes = kListOff + kMaxQueryBlock * 16;
-  static_assert(kSlabBytes >= 2 * kMaxQueryBlock * 4, "slab doubles as scan scratch");
+  static_assert(kSlabBytes >= kMaxQueryBlock * 4, "slab doubles as scan scratch");
 };
 
 // Exclusive prefix sum over a[0..n) in LDS by one wave, in place; returns the total.
@@ -79,32 +79,59 @@ __device__ int wave_exclusive_scan(int* a, int n) {
   return __shfl(incl, 63, 64);
 }
 
+// Records of one 32-slot tile as the lane needs them.  MFMA row m (the A
+// operand's lane m = l32) takes record base + pi(m), pi(8i + 4h + r) =
+// 16h + 4i + r, so that accumulator register 4i + r of a lane in half h is the
+// record base + 16h + 4i + r: four aligned 16-byte loads give a lane the keys
+// (and four the dI) of its 16 rows.
+// Entries past a range's end are sinks (key one past the range), so a tile
+// needs no bounds checks: sink rows land in the slab's scratch row RK.
+struct Tile {
+  uint2 w;      // sign words of record base + pi(l32)
+  int ka;       // key of record base + pi(l32)
+  int4 key[4];  // keys of records base + 16*half + 4*i + (0..3)
+  float4 di[4];  // their dI
+};
+
 template <int NH, int D>
 __global__ __launch_bounds__(64 * DkShape<D>::NW, 1) void dk_range_kernel(Problem P) {
   using S = DkShape<D>;
+  constexpr int KS = NH * 2;  // 16-deep k-steps over the heads
   constexpr int HP = NH * 32;
   constexpr int NTH = 64 * S::NW;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   float* slab = reinterpret_cast<float*>(lds);
-  u32x4_t* lut = reinterpret_cast<u32x4_t*>(lds + S::kLutOff);
   int4* list = reinterpret_cast<int4*>(lds + S::kListOff);
   __shared__ int nne_s;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
   const int wv = tid >> 6;
-  const int l16 = lane & 15;
-  const int grp = lane >> 4;
-  const int R = blockIdx.x;
-  const int qb = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  // Workgroup i is dispatched to XCD i % 8.  Consecutive logical ids (the key
+  // ranges of one query block) are given to workgroups of one XCD, so the
+  // (w*q)^T rows that every range of the block reads are fetched into that
+  // XCD's L2 once and hit there for the other ranges.
+  int R, qb;
+  int64_t b;
+  {
+    const int n = int(gridDim.x);
+    const int i = int(blockIdx.x);
+    const int x = i % kXcds, k = i / kXcds;
+    const int per = n / kXcds, rem = n % kXcds;
+    const int logical = x * per + (x < rem ? x : rem) + k;
+    R = logical % int(P.NR);
+    qb = (logical / int(P.NR)) % int(P.NQB);
+    b = logical / int(P.NR * P.NQB);
+  }
   const int RK = S::RK;
   const int R0 = R * RK;
   const int nkeys = int(P.S_k - R0 < RK ? P.S_k - R0 : RK);
   const int64_t t0 = int64_t(qb) * P.QBS;
   const int nq = int((t0 + P.QBS < P.S_q ? t0 + P.QBS : P.S_q) - t0);
 
-  // ---- the block's queries that have slots in this range, with tile offsets
+  // ---- the block's queries that have records in this range ------------------
   {
     int* flag = reinterpret_cast<int*>(lds);  // scratch in the slab area
     int4 mine[(kMaxQueryBlock + NTH - 1) / NTH];
@@ -113,11 +140,9 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 1) void dk_range_kernel(Proble
       const int i = tid + u * NTH;
       if (i < nq) {
         const int64_t row = b * P.S_q + t0 + i;
-        const int* offrow = P.off + row * (P.NR + 1);
-        const int rb = offrow[R], re = offrow[R + 1];
-        const int nt = (re - rb + kTile - 1) / kTile;
-        mine[u] = make_int4(int(row), rb, re, nt);
-        flag[i] = nt > 0 ? 1 : 0;
+        const int2 fe = reinterpret_cast<const int2*>(P.offs)[row * P.NR + R];
+        mine[u] = make_int4(int(row), fe.x, fe.y, 0);
+        flag[i] = fe.y > fe.x ? 1 : 0;
       }
     }
     __syncthreads();
@@ -129,154 +154,140 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 1) void dk_range_kernel(Proble
 #pragma unroll
     for (int u = 0; u < (kMaxQueryBlock + NTH - 1) / NTH; ++u) {
       const int i = tid + u * NTH;
-      if (i < nq && mine[u].w > 0) list[flag[i]] = mine[u];
-    }
-    __syncthreads();
-    if (wv == 0) {
-      const int nne = nne_s;
-      for (int i = lane; i < nne; i += 64) flag[i] = list[i].w;
-      wave_lds_sync();
-      wave_exclusive_scan(flag, nne);
-      for (int i = lane; i < nne; i += 64) list[i].w = flag[i];  // w := first tile
+      if (i < nq && mine[u].z > mine[u].y) list[flag[i]] = mine[u];
     }
     __syncthreads();
   }
   const int nne = nne_s;
 
-  for (int i = tid; i < RK * S::kPitch; i += NTH) slab[i] = 0.f;
-  // byte -> 8 bf16: bit e of the byte is 1.0 (0x3f80) or 0
-  for (int e = tid; e < 256; e += NTH) {
-    uint32_t wd[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      wd[i] = (((e >> (2 * i)) & 1) ? 0x3f80u : 0u) | (((e >> (2 * i + 1)) & 1) ? 0x3f800000u : 0u);
-    lut[e] = u32x4_t{wd[0], wd[1], wd[2], wd[3]};
-  }
+  for (int i = tid; i < (RK + 1) * D; i += NTH) slab[i] = 0.f;
+  int* stamp = reinterpret_cast<int*>(lds + S::kStampOff) + wv * RK;
+  for (int i = lane; i < RK; i += 64) stamp[i] = 0;
   __syncthreads();
 
-  int* stamp = reinterpret_cast<int*>(lds + S::kStampOff) + wv * RK;
-  const int d0 = wv * S::DW;
+  const int col = 32 * wv + l32;  // the lane's slab column
+  // A-operand expansion: element pair j of k-step ks sits at bits q and q + 16
+  // of the sign word shifted right by 8*(ks & 1), q = 4*half + j
+  uint32_t emask[4], emul[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    emask[j] = 0x10001u << (4 * half + j);
+    emul[j] = 0x3f80u >> (4 * half + j);
+  }
+  const int pim = 16 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
 
-  // A operand: (w*q)^T, lane holds d = d0 + 16*mt + l16, h = 32*ks + 8*grp + e
-  auto load_qt = [&](int row, u32x4_t (&a)[S::MT][NH]) {
-    const uint16_t* qtrow = P.qt + int64_t(row) * D * HP;
+  // B operand: (w*q)^T, lane holds d = col, h = 16*ks + 8*half + e
+  auto load_qt = [&](int row, u32x4_t (&a)[KS]) {
+    const uint16_t* qtrow = P.qt + int64_t(row) * D * HP + col * HP + 8 * half;
 #pragma unroll
-    for (int mt = 0; mt < S::MT; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < NH; ++ks)
-        a[mt][ks] = *reinterpret_cast<const u32x4_t*>(qtrow + (d0 + 16 * mt + l16) * HP + 32 * ks +
-                                                      8 * grp);
+    for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const u32x4_t*>(qtrow + 16 * ks);
   };
-  // record of slot l16 of a tile; index past the range end reads a row-tail entry
-  auto load_rec = [&](int row, int idx, int end, bool& valid) -> int4 {
-    valid = idx < end;
-    const int i = valid ? idx : int(P.row_len);
-    return P.rec[int64_t(row) * P.rec_stride + i];
-  };
-
-  // one 16-slot tile: the lane's record r (slot l16), valid flag vm, A operand qa
-  auto process = [&](const int4& r, bool vm, const u32x4_t (&qa)[S::MT][NH]) {
-    const int key = r.x;
-    const float dI = __int_as_float(r.y);
-    u32x4_t bop[NH];
+  // records of the tile starting at `base` (at most 31 entries past the
+  // range's end: inside its sink entries)
+  auto load_tile = [&](int row, int base) -> Tile {
+    Tile tl;
+    const int64_t ro = int64_t(row) * P.rec_stride;
+    const int ia = base + pim;
+    tl.w = reinterpret_cast<const uint2*>(P.rmask)[ro + ia];
+    tl.ka = P.rkey[ro + ia];
 #pragma unroll
-    for (int ks = 0; ks < NH; ++ks) {
-      const uint32_t word = vm ? uint32_t(ks == 0 ? r.z : r.w) : 0u;
-      bop[ks] = lut[(word >> (8 * grp)) & 0xffu];
+    for (int i = 0; i < 4; ++i) {
+      const int ir = base + 16 * half + 4 * i;
+      tl.key[i] = *reinterpret_cast<const int4*>(P.rkey + ro + ir);
+      tl.di[i] = *reinterpret_cast<const float4*>(P.rdi + ro + ir);
     }
-    // are the tile's keys pairwise distinct?
-    if (lane < kTile && vm) stamp[key - R0] = lane;
-    wave_lds_sync();
-    const bool clash = lane < kTile && vm && stamp[key - R0] != lane;
-    const bool distinct = ballot(clash) == 0;
+    return tl;
+  };
 
-    f32x4_t acc[S::MT];
-#pragma unroll
-    for (int mt = 0; mt < S::MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NH; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < S::MT; ++mt) acc[mt] = mfma16(qa[mt][ks], bop[ks], acc[mt]);
+  int tile_id = 0;
+  // one tile of records tl with B operand qa
+  auto process = [&](const Tile& tl, const u32x4_t (&qa)[KS]) {
+    // are the tile's keys pairwise distinct?  (stamps are per wave; sinks,
+    // key - R0 == RK, are not counted)
+    ++tile_id;
+    bool clash = false;
+    if (half == 0 && tl.ka - R0 < RK) clash = atomicExch(&stamp[tl.ka - R0], tile_id) == tile_id;
 
-    // lane holds slot l16, d = d0 + 16*mt + 4*grp + (0..3)
-    float* rowp = slab + (key - R0) * S::kPitch + d0 + 4 * grp;
-    if (distinct) {
-      if (vm) {
-        float4 old[S::MT];
+    f32x16_t acc = f32x16_t{};
 #pragma unroll
-        for (int mt = 0; mt < S::MT; ++mt) old[mt] = *reinterpret_cast<const float4*>(rowp + 16 * mt);
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t word = (ks < 2 ? tl.w.x : tl.w.y) >> (8 * (ks & 1));
+      u32x4_t av;
 #pragma unroll
-        for (int mt = 0; mt < S::MT; ++mt) {
-          float4 v = old[mt];
-          v.x = fmaf(dI, acc[mt][0], v.x);
-          v.y = fmaf(dI, acc[mt][1], v.y);
-          v.z = fmaf(dI, acc[mt][2], v.z);
-          v.w = fmaf(dI, acc[mt][3], v.w);
-          *reinterpret_cast<float4*>(rowp + 16 * mt) = v;
-        }
-      }
+      for (int j = 0; j < 4; ++j) av[j] = __umul24(word & emask[j], emul[j]);
+      acc = mfma32(av, qa[ks], acc);
+    }
+
+    // accumulator register 4i + r: record base + 16*half + 4i + r, column col
+    const int cbase = col - R0 * D;
+    int addr[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      addr[4 * i + 0] = tl.key[i].x * D + cbase;
+      addr[4 * i + 1] = tl.key[i].y * D + cbase;
+      addr[4 * i + 2] = tl.key[i].z * D + cbase;
+      addr[4 * i + 3] = tl.key[i].w * D + cbase;
+    }
+    const float dv[16] = {tl.di[0].x, tl.di[0].y, tl.di[0].z, tl.di[0].w, tl.di[1].x, tl.di[1].y,
+                          tl.di[1].z, tl.di[1].w, tl.di[2].x, tl.di[2].y, tl.di[2].z, tl.di[2].w,
+                          tl.di[3].x, tl.di[3].y, tl.di[3].z, tl.di[3].w};
+    if (ballot(clash) == 0) {
+      float old[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) old[k] = slab[addr[k]];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) slab[addr[k]] = fmaf(dv[k], acc[k], old[k]);
     } else {
-      // ordered path: one slot of the tile at a time
-      for (int m = 0; m < kTile; ++m) {
-        if (l16 == m && vm) {
-#pragma unroll
-          for (int mt = 0; mt < S::MT; ++mt) {
-            float4 v = *reinterpret_cast<const float4*>(rowp + 16 * mt);
-            v.x = fmaf(dI, acc[mt][0], v.x);
-            v.y = fmaf(dI, acc[mt][1], v.y);
-            v.z = fmaf(dI, acc[mt][2], v.z);
-            v.w = fmaf(dI, acc[mt][3], v.w);
-            *reinterpret_cast<float4*>(rowp + 16 * mt) = v;
-          }
+      // ordered path: one slab row (one register of one half-wave) at a time
+      for (int k = 0; k < 16; ++k) {
+        for (int hh = 0; hh < 2; ++hh) {
+          if (half == hh) slab[addr[k]] = fmaf(dv[k], acc[k], slab[addr[k]]);
+          wave_lds_sync();
         }
-        wave_lds_sync();
       }
     }
-    wave_lds_sync();
   };
-  // all tiles of one query; f/fv is the record of its first tile, loaded a
-  // query earlier.  Records are prefetched one tile ahead with the loop
-  // unrolled by two so that no loaded register is copied (a copy would wait
-  // for the load).
-  auto run_query = [&](const int4& e, const u32x4_t (&qa)[S::MT][NH], const int4& f, bool fv) {
+  // all tiles of one query; f is its first tile, loaded a query earlier.
+  // Tiles are prefetched one ahead with the loop unrolled by two so that no
+  // loaded register is copied (a copy would wait for the load).
+  auto run_query = [&](const int4& e, const u32x4_t (&qa)[KS], const Tile& f) {
     const int ntl = (e.z - e.y + kTile - 1) / kTile;
-    bool vb;
-    int4 rb = load_rec(e.x, e.y + kTile + l16, e.z, vb);
-    process(f, fv, qa);
+    const int last = e.y + kTile * (ntl - 1);
+    auto tbase = [&](int tt) { return e.y + kTile * tt < last ? e.y + kTile * tt : last; };
+    Tile tb = load_tile(e.x, tbase(1));
+    process(f, qa);
     for (int tt = 1; tt < ntl; tt += 2) {
-      bool va;
-      const int4 ra = load_rec(e.x, e.y + kTile * (tt + 1) + l16, e.z, va);
-      process(rb, vb, qa);
-      rb = load_rec(e.x, e.y + kTile * (tt + 2) + l16, e.z, vb);
-      if (tt + 1 < ntl) process(ra, va, qa);
+      const Tile ta = load_tile(e.x, tbase(tt + 1));
+      process(tb, qa);
+      tb = load_tile(e.x, tbase(tt + 2));
+      if (tt + 1 < ntl) process(ta, qa);
     }
   };
 
   if (nne > 0) {
     // queries alternate between two operand sets, each loaded one query ahead
-    u32x4_t qa0[S::MT][NH], qa1[S::MT][NH];
-    int4 f0, f1;
-    bool fv0, fv1;
+    u32x4_t qa0[KS], qa1[KS];
+    Tile f0, f1;
     {
       const int4 e0 = list[0];
       const int4 e1 = list[nne > 1 ? 1 : 0];
       load_qt(e0.x, qa0);
-      f0 = load_rec(e0.x, e0.y + l16, e0.z, fv0);
+      f0 = load_tile(e0.x, e0.y);
       load_qt(e1.x, qa1);
-      f1 = load_rec(e1.x, e1.y + l16, nne > 1 ? e1.z : 0, fv1);
+      f1 = load_tile(e1.x, e1.y);
     }
     for (int qi = 0; qi < nne; qi += 2) {
-      run_query(list[qi], qa0, f0, fv0);
+      run_query(list[qi], qa0, f0);
       {
         const int4 e2 = list[qi + 2 < nne ? qi + 2 : nne - 1];
         load_qt(e2.x, qa0);
-        f0 = load_rec(e2.x, e2.y + l16, qi + 2 < nne ? e2.z : 0, fv0);
+        f0 = load_tile(e2.x, e2.y);
       }
-      if (qi + 1 < nne) run_query(list[qi + 1], qa1, f1, fv1);
+      if (qi + 1 < nne) run_query(list[qi + 1], qa1, f1);
       {
         const int4 e3 = list[qi + 3 < nne ? qi + 3 : nne - 1];
         load_qt(e3.x, qa1);
-        f1 = load_rec(e3.x, e3.y + l16, qi + 3 < nne ? e3.z : 0, fv1);
+        f1 = load_tile(e3.x, e3.y);
       }
     }
   }
@@ -285,7 +296,7 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 1) void dk_range_kernel(Proble
   float* dst = P.slab + ((b * P.NQB + qb) * (P.NR * RK) + R0) * D;
   for (int i = tid; i < nkeys * (D / 4); i += NTH) {
     const int kr = i / (D / 4), c4 = i % (D / 4);
-    const float4 v = *reinterpret_cast<const float4*>(slab + kr * S::kPitch + 4 * c4);
+    const float4 v = *reinterpret_cast<const float4*>(slab + kr * D + 4 * c4);
     *reinterpret_cast<float4*>(dst + kr * D + 4 * c4) = v;
   }
 }
@@ -315,7 +326,7 @@ __global__ __launch_bounds__(256) void dk_sum_kernel(Problem P) {
 template <int NH, int D>
 hipError_t launch_dk_t(const Problem& P, hipStream_t stream) {
   using S = DkShape<D>;
-  const dim3 grid(unsigned(P.NR), unsigned(P.NQB), unsigned(P.B));
+  const dim3 grid(unsigned(P.NR * P.NQB * P.B));
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&dk_range_kernel<NH, D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::kBytes);
   if (err != hipSuccess) return err;

@@ -1,8 +1,8 @@
 // Launch sequence of the lightning-indexer backward on gfx950.
 //
 //   two-pass route (default, bitwise deterministic):
-//     row_kernel      one wave per query row: dQ, dW, slot records (key, dI,
-//                     sign mask of S over h), (w*q)^T
+//     row_export_kernel one wave per (query row, 32 heads): dQ, dW, slot records
+//                     (key, dI, sign mask of S over h), (w*q)^T
 //     dk_range_kernel one workgroup per (key range, query block): dK slabs in LDS
 //     dk_sum_kernel   d_k = fixed-order sum of the query-block slabs
 //   atomic route:
@@ -40,11 +40,13 @@ hipError_t launch(Problem P, void* workspace, hipStream_t stream) {
     return launch_rows(P, stream);
   }
   char* ws = static_cast<char*>(workspace);
-  P.rec = reinterpret_cast<int4*>(ws + L.off_rec);
-  P.off = reinterpret_cast<int*>(ws + L.off_off);
+  P.rkey = reinterpret_cast<int*>(ws + L.off_rkey);
+  P.rdi = reinterpret_cast<float*>(ws + L.off_rdi);
+  P.rmask = reinterpret_cast<uint32_t*>(ws + L.off_rmask);
+  P.offs = reinterpret_cast<int*>(ws + L.off_offs);
   P.qt = reinterpret_cast<uint16_t*>(ws + L.off_qt);
   P.slab = reinterpret_cast<float*>(ws + L.off_slab);
-  if ((err = launch_rows(P, stream)) != hipSuccess) return err;
+  if ((err = launch_rows_export(P, stream)) != hipSuccess) return err;
   return launch_dk(P, stream);
 }
 

@@ -19,13 +19,9 @@
 // register axis) is read transposed from a wave-private LDS tile with
 // ds_read_b64_tr_b16.  dQ' accumulates in registers over the whole row.
 //
-// The dK term has two routes:
-//  * two-pass (default): the wave exports, per chunk, the 64 ballots of
-//    [S > 0] (the sign mask that, with dI, fixes G'), one record {key, dI, slot}
-//    per valid slot grouped by key range, and once per row (w*q)^T in bf16.  The
-//    range kernel rebuilds C = G'^T Q' from them and reduces it in LDS.
-//  * atomic: GEMM3  C[j,d] = G'[h,j] Q'[h,d] (M=j N=d K=h, G' read transposed
-//    from LDS) and an fp32 atomic add of every C row into dK.
+// dK (this file is the atomic route): GEMM3  C[j,d] = G'[h,j] Q'[h,d]
+// (M=j N=d K=h, G' read transposed from LDS) and an fp32 atomic add of every C
+// row into dK.  The two-pass route has its own row kernel.
 //
 // Loads are software-pipelined one chunk ahead: the slot data (ids, I, p) of
 // chunk c+2 and the K rows of chunk c+1 are in flight while chunk c computes.
@@ -40,7 +36,6 @@
 namespace ibwd {
 namespace {
 
-constexpr int kMaxRowRanges = 1024;  // key ranges a row can be bucketed into
 
 template <int D>
 struct RowLds {
@@ -52,8 +47,7 @@ struct RowLds {
   static constexpr int kGOff = kKArea;
   static constexpr int kStageOff = kGOff + 64 * kGPitch;
   static constexpr int kStageBytes = kSlots * 8;  // dI (fp32) + key (int32)
-  static constexpr int kCursorOff = kStageOff + 2 * kStageBytes;
-  static constexpr int kBytes = kCursorOff + kMaxRowRanges * 4;
+  static constexpr int kBytes = kStageOff + 2 * kStageBytes;
 };
 
 // Slot data of one chunk as loaded (lane l holds slot l%32).
@@ -63,53 +57,11 @@ struct Raw {
   float p;
 };
 
-// Exclusive prefix sum of a[0..n) in LDS, in place; returns the total.
-__device__ int wave_exclusive_scan(int* a, int n) {
-  const int lane = threadIdx.x & 63;
-  const int per = (n + 63) / 64;
-  const int s0 = lane * per;
-  const int s1 = s0 + per < n ? s0 + per : n;
-  int s = 0;
-  for (int i = s0; i < s1; ++i) s += a[i];
-  int incl = s;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
-  }
-  int run = incl - s;
-  wave_lds_sync();
-  for (int i = s0; i < s1; ++i) {
-    const int v = a[i];
-    a[i] = run;
-    run += v;
-  }
-  wave_lds_sync();
-  return __shfl(incl, 63, 64);
-}
-
-// Lanes of the wave whose range equals this lane's (valid lanes only), from
-// nbits ballots of the range bits.
-__device__ __forceinline__ uint64_t same_range_lanes(bool valid, int r, int nbits) {
-  uint64_t same = ballot(valid);
-  for (int b = 0; b < nbits; ++b) {
-    const uint64_t bb = ballot(valid && ((r >> b) & 1));
-    same &= ((r >> b) & 1) ? bb : ~bb;
-  }
-  return same;
-}
-
-// Lanes 2*idx and 2*idx+1 of the result take the two halves of a ballot.
-__device__ __forceinline__ uint32_t put_ballot(uint32_t word, uint64_t bal, int idx) {
-  word = write_lane(word, uint32_t(bal), 2 * idx);
-  return write_lane(word, uint32_t(bal >> 32), 2 * idx + 1);
-}
-
-template <int NH, int D, bool DENSE, int ROUTE>
+template <int NH, int D, bool DENSE>
 __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
   constexpr int ND = D / 32;  // 32-wide d tiles
   constexpr int KD = D / 16;  // 16-deep d steps (GEMM1 K)
   constexpr int KH = NH * 2;  // 16-deep h steps (GEMM3 K)
-  constexpr int HP = NH * 32;
   using L = RowLds<D>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
 
@@ -133,9 +85,6 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
   const int32_t* idrow = DENSE ? nullptr : P.ids + r * P.row_len;
   const uint16_t* kb = P.k + b * P.S_k * D;
   const int S_k = int(P.S_k);
-  const int RK = int(P.RK);
-  const int NR = int(P.NR);
-  int* cursor = reinterpret_cast<int*>(lds + L::kCursorOff);
 
   auto key_of = [&](int j, int id) -> int {
     if (j >= n) return -1;
@@ -143,57 +92,12 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
     return (id >= 0 && id < S_k) ? id : -1;
   };
 
-  // ---- softmax statistics over the valid slots (online max / sum), and for
-  //      the two-pass route the per-range slot counts of the row --------------
-  int nbits = 0;
-  if (ROUTE == kDkTwoPass && !DENSE) {
-    while ((1 << nbits) < NR) ++nbits;
-    for (int i = lane; i < NR; i += 64) cursor[i] = 0;
-    wave_lds_sync();
-  }
-  float m = -INFINITY, z = 0.f;
-  for (int j0 = 0; j0 < n; j0 += 64) {
-    const int j = j0 + lane;
-    const int key = j < n ? key_of(j, DENSE ? 0 : idrow[j]) : -1;
-    const bool valid = key >= 0;
-    if (valid) {
-      const float v = P.sm_scale * Irow[j];
-      if (v > m) {
-        z = z * expf(m - v) + 1.f;
-        m = v;
-      } else {
-        z += expf(v - m);
-      }
-    }
-    if (ROUTE == kDkTwoPass && !DENSE) {
-      const int rg = valid ? key / RK : 0;
-      const uint64_t same = same_range_lanes(valid, rg, nbits);
-      if (valid && (same & lanemask_lt()) == 0) cursor[rg] += __popcll(same);
-      wave_lds_sync();
-    }
-  }
-  {
-    const float mw = wave_max(m);
-    z = (m > -INFINITY) ? z * expf(m - mw) : 0.f;
-    z = wave_sum(z);
-    m = mw;
-  }
-  const float invZ = z > 0.f ? 1.f / z : 0.f;
+  // ---- softmax statistics over the valid slots ---------------------------------
+  const float c2 = P.sm_scale * 1.4426950408889634f;  // base-2 logit scale
+  const float2 st = row_softmax_stats(
+      n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [](int) {});
+  const float m2 = st.x, invZ = st.y;
   const float coef = P.grad_loss * P.sm_scale;
-
-  if (ROUTE == kDkTwoPass) {
-    int* offrow = P.off + r * (P.NR + 1);
-    if (DENSE) {
-      for (int i = lane; i <= NR; i += 64) {
-        const int64_t o = int64_t(i) * RK;
-        offrow[i] = int(o < n ? o : n);
-      }
-    } else {
-      const int total = wave_exclusive_scan(cursor, NR);
-      for (int i = lane; i < NR; i += 64) offrow[i] = cursor[i];
-      if (lane == 0) offrow[NR] = total;
-    }
-  }
 
   // ---- per-row operands ------------------------------------------------------
   const float* wrow = P.w + r * P.H;
@@ -215,10 +119,9 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
                           : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  // Q'[h][d] = bf16(w_h * q[h][d]) staged in LDS rows h; read back transposed:
-  // lane d = 32*nd + l32, h = 16*ks + 8*half + e.  The atomic route keeps it
-  // as GEMM3's B operand, the two-pass route stores it as (w*q)^T.
-  u32x4_t qb3[ROUTE == kDkAtomic ? ND : 1][KH];
+  // Q'[h][d] = bf16(w_h * q[h][d]) staged in LDS rows h; read back transposed
+  // (lane d = 32*nd + l32, h = 16*ks + 8*half + e) as GEMM3's B operand.
+  u32x4_t qb3[ND][KH];
   {
     unsigned char* qs = lds;
 #pragma unroll
@@ -234,19 +137,13 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
       }
     }
     wave_lds_sync();
-    uint16_t* qtrow = (ROUTE == kDkTwoPass) ? P.qt + r * D * HP : nullptr;
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {
       const int col0 = 32 * nd + 16 * ((lane >> 4) & 1);
 #pragma unroll
       for (int ks = 0; ks < KH; ++ks) {
         const int r0 = 16 * ks + 8 * half;
-        const u32x4_t v = lds_tr8(qs, L::kPitch, r0, r0 + 4, col0);
-        if (ROUTE == kDkAtomic) {
-          qb3[ROUTE == kDkAtomic ? nd : 0][ks] = v;
-        } else {
-          *reinterpret_cast<u32x4_t*>(qtrow + (32 * nd + l32) * HP + r0) = v;
-        }
+        qb3[nd][ks] = lds_tr8(qs, L::kPitch, r0, r0 + 4, col0);
       }
     }
     wave_lds_sync();
@@ -270,7 +167,7 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
   auto finalize = [&](int c, const Raw& v, float& dI) -> int {
     const int j = c * kSlots + l32;
     const int key = key_of(j, v.id);
-    dI = key >= 0 ? coef * (expf(P.sm_scale * v.I - m) * invZ - v.p) : 0.f;
+    dI = key >= 0 ? slot_dI(v.I, v.p, c2, m2, invZ, coef) : 0.f;
     // lanes l and l+32 hold the same slot and store the same values: no branch
     reinterpret_cast<float*>(stage_ptr(c))[l32] = dI;
     reinterpret_cast<int*>(stage_ptr(c) + kSlots * 4)[l32] = key;
@@ -314,21 +211,13 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
   }
 
   unsigned char* gs = lds + L::kGOff;
-  int4* recrow = (ROUTE == kDkTwoPass) ? P.rec + r * P.rec_stride : nullptr;
-  float* dkb = (ROUTE == kDkAtomic) ? P.dk + b * P.S_k * D : nullptr;
+  float* dkb = P.dk + b * P.S_k * D;
 
-  // The record of chunk c is stored at the top of iteration c+1, right after
-  // the one wait of the iteration: gfx9's vmcnt also counts stores, and a store
-  // in flight makes the next wait on a load a full drain, so every global
-  // access is issued early and waited for only at the end of the iteration.
-  int prev_pos = row_len + l32;  // the first store goes to the row's tail
-  int4 prev_rec = make_int4(-1, 0, 0, 0);
   for (int c = 0; c < nchunks; ++c) {
     // slot data of chunk c+1 (loaded one chunk ago) -> stage ring; its K rows
     // and the slot data of chunk c+2 go in flight
     float dIn;
     const int key_n = finalize(c + 1, raw_next, dIn);
-    if (ROUTE == kDkTwoPass) recrow[prev_pos] = prev_rec;
     u32x4_t knext[KD];
     gather(key_n, knext);
     raw_next = load_raw(c + 2);
@@ -361,7 +250,6 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
       dIv[i][3] = v.w;
     }
     uint32_t gp[NH][4][2];
-    uint32_t maskword = 0;
 #pragma unroll
     for (int nt = 0; nt < NH; ++nt) {
 #pragma unroll
@@ -373,20 +261,12 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
           const bool pos = sv > 0.f;
           g[rr] = pos ? dIv[i][rr] : 0.f;
           dw_acc[nt] = fmaf(g[rr], sv, dw_acc[nt]);
-          if (ROUTE == kDkTwoPass) {
-            // ballot word 2*idx + half = bits over h = 32*nt + (0..31) of slot
-            // 8*i + 4*half + rr, idx = 16*nt + 4*i + rr
-            const uint64_t bal = ballot(pos);
-            maskword = put_ballot(maskword, bal, 16 * nt + 4 * i + rr);
-          }
         }
         gp[nt][i][0] = pack_bf16(g[0], g[1]);
         gp[nt][i][1] = pack_bf16(g[2], g[3]);
-        if (ROUTE == kDkAtomic) {
-          // G' tile in LDS: row h, slots 8*i + 4*half .. +3
-          *reinterpret_cast<uint2*>(gs + (l32 + 32 * nt) * L::kGPitch + (8 * i + 4 * half) * 2) =
-              make_uint2(gp[nt][i][0], gp[nt][i][1]);
-        }
+        // G' tile in LDS: row h, slots 8*i + 4*half .. +3
+        *reinterpret_cast<uint2*>(gs + (l32 + 32 * nt) * L::kGPitch + (8 * i + 4 * half) * 2) =
+            make_uint2(gp[nt][i][0], gp[nt][i][1]);
       }
     }
 
@@ -409,31 +289,7 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
       }
     }
 
-    if (ROUTE == kDkTwoPass) {
-      // ---- export: one record {key, dI, sign bits of h 0..31, of h 32..63} per
-      //      valid slot.  Lane w of maskword holds ballot word w; slot j of the
-      //      chunk finds its words at 2*(4*(j/8) + j%4) + (j/4)%2 (+32 for h >= 32).
-      const int key = sk[l32];
-      const bool valid = lane < kSlots && key >= 0;
-      const int j = c * kSlots + l32;
-      const int w0 = 2 * (4 * (l32 >> 3) + (l32 & 3)) + ((l32 >> 2) & 1);
-      const uint32_t m0 = uint32_t(__shfl(int(maskword), w0, 64));
-      const uint32_t m1 = NH == 2 ? uint32_t(__shfl(int(maskword), w0 + 32, 64)) : 0u;
-      int pos;
-      if (DENSE) {
-        pos = j;
-      } else {
-        const int rg = valid ? key / RK : 0;
-        const uint64_t same = same_range_lanes(valid, rg, nbits);
-        const int base = valid ? cursor[rg] : 0;
-        pos = base + __popcll(same & lanemask_lt());
-        wave_lds_sync();
-        if (valid && (same & lanemask_lt()) == 0) cursor[rg] = base + __popcll(same);
-      }
-      // padding lanes and the upper half-wave store into the row's tail
-      prev_pos = valid ? pos : row_len + l32;
-      prev_rec = make_int4(key, __float_as_int(sd[l32]), int(m0), int(m1));
-    } else {
+    {
       wave_lds_sync();  // G' tile complete
       // ---- GEMM3: C[j][d] = G'^T[j][h] Q'[h][d], then the dK scatter ----------
       u32x4_t ga[KH];
@@ -456,7 +312,7 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
         f32x16_t cacc = f32x16_t{};
 #pragma unroll
         for (int ks = 0; ks < KH; ++ks)
-          cacc = mfma32(ga[ks], qb3[ROUTE == kDkAtomic ? nd : 0][ks], cacc);
+          cacc = mfma32(ga[ks], qb3[nd][ks], cacc);
         const int d = l32 + 32 * nd;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -475,8 +331,6 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
     store_k(c + 1, knext, key_n);
     wave_lds_sync();
   }
-
-  if (ROUTE == kDkTwoPass) recrow[prev_pos] = prev_rec;
 
   // ---- row epilogue: dQ = w * dQ', dW -----------------------------------------
   float* dqrow = P.dq + r * P.H * D;
@@ -507,10 +361,7 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
 template <int NH, int D, bool DENSE>
 hipError_t launch_rows_t(const Problem& P, hipStream_t stream) {
   const dim3 grid(unsigned(P.B * P.S_q));
-  if (P.route == kDkAtomic)
-    row_kernel<NH, D, DENSE, kDkAtomic><<<grid, 64, 0, stream>>>(P);
-  else
-    row_kernel<NH, D, DENSE, kDkTwoPass><<<grid, 64, 0, stream>>>(P);
+  row_kernel<NH, D, DENSE><<<grid, 64, 0, stream>>>(P);
   return hipGetLastError();
 }
 

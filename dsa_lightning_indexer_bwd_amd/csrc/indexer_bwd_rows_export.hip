@@ -1,0 +1,427 @@
+// Row kernel of the two-pass route for gfx950: one wave per (query row, group
+// of 32 heads), two waves per SIMD.
+//
+// Math per query row t (NVIDIA/cudnn-frontend PR #730: the harness' fp64
+// `ref_grads` and the kernel-1 score-gradient contract):
+//   dI_j    = grad_loss*sm_scale*(softmax_V(sm_scale*I)_j - p_j)   (0 on padding)
+//   S[h,j]  = q[t,h,:] . k[id_j,:]
+//   G'[h,j] = dI_j * [S[h,j] > 0]          (G = w[t,h] * G')
+//   dW[t,h] = sum_j G'[h,j] * S[h,j]
+//   dQ[t,h,:] = w[t,h] * sum_j G'[h,j] * k[id_j,:]
+// and, for the range kernel that finishes dK, per valid slot a record
+// {key, dI, the sign bits [S[h,j] > 0] of every h} grouped by key range, and
+// (w*q)^T of the row.
+//
+// Splitting the 64 heads over two independent waves halves every per-wave
+// register array (dQ' accumulators, Q, the score tile), so a wave fits in 256
+// registers and two waves share each SIMD: one wave's VALU work (mask, G', dW)
+// overlaps the other's MFMA work.  The waves of one row repeat the cheap
+// per-row work (softmax statistics, record ranking) and need no
+// synchronisation with each other.
+//
+// Per chunk of 32 slots:
+//   GEMM1  S^T[j,h]  = K_g[j,:] . Q[h,:]     v_mfma 32x32x16, M=j N=h K=d; K_g
+//          straight from the gather registers (GEMM1's A layout)
+//   GEMM2  dQ'[h,d] += G'[h,j] K_g[j,d]      M=h N=d K=j; G' from GEMM1's
+//          accumulators, K_g^T read transposed from a wave-private LDS tile
+// The head of lane l32 in GEMM1's N dimension is 32*g + rotl5(l32), so the
+// ballot of [S > 0] over the wave is directly the record's sign word in the
+// bit order the range kernel expands with two VALU operations per pair.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace ibwd {
+namespace {
+
+template <int D>
+struct ExportLds {
+  static constexpr int kPitch = D * 2 + 16;  // bytes per K / Q' row (bank spread)
+  static constexpr int kTile = kSlots * kPitch;  // K chunk; Q' staging (32 rows) aliases it
+  static constexpr int kStageOff = kTile;
+  static constexpr int kStageBytes = kSlots * 8;  // dI (fp32) + key (int32)
+  static constexpr int kCursorOff = kStageOff + 2 * kStageBytes;
+  static constexpr int kBytes = kCursorOff + kMaxRanges * 4;
+};
+
+struct Raw {
+  int id;
+  float I;
+  float p;
+};
+
+__device__ __forceinline__ int rotl5(int b) { return ((b << 1) | (b >> 4)) & 31; }
+
+// Lanes of the wave whose range equals this lane's (valid lanes only), from
+// nbits ballots of the range bits.
+__device__ __forceinline__ uint64_t same_range_lanes(bool valid, int r, int nbits) {
+  uint64_t same = ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const uint64_t bb = ballot(valid && ((r >> b) & 1));
+    same &= ((r >> b) & 1) ? bb : ~bb;
+  }
+  return same;
+}
+
+template <int D, bool DENSE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void row_export_kernel(
+    Problem P) {
+  constexpr int KD = D / 16;  // GEMM1 k-steps over d
+  constexpr int ND = D / 32;  // GEMM2 32-wide d tiles
+  using L = ExportLds<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
+
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+  const int H = int(P.H);
+  const int NG = int(P.HP / 32);
+  const int HP = int(P.HP);
+  const int g = int(blockIdx.x % unsigned(NG));
+  const int64_t ridx = int64_t(blockIdx.x / unsigned(NG));
+  // dense rows are visited longest first
+  const int64_t r = DENSE ? (P.B * P.S_q - 1 - ridx) : ridx;
+  const int64_t b = r / P.S_q;
+  const int64_t t = r % P.S_q;
+  const int row_len = int(P.row_len);
+  int n = row_len;
+  if (DENSE) {
+    const int64_t last = t + P.q_offset;
+    n = last < 0 ? 0 : int(last + 1 < P.S_k ? last + 1 : P.S_k);
+  }
+  const float* Irow = P.I + r * P.row_len;
+  const float* prow = P.p + r * P.row_len;
+  const int32_t* idrow = DENSE ? nullptr : P.ids + r * P.row_len;
+  const uint16_t* kb = P.k + b * P.S_k * D;
+  const int S_k = int(P.S_k);
+  const int RK = int(P.RK);
+  const int NR = int(P.NR);
+  int* cursor = reinterpret_cast<int*>(lds + L::kCursorOff);
+
+  auto key_of = [&](int j, int id) -> int {
+    if (j >= n) return -1;
+    if (DENSE) return j;
+    return (id >= 0 && id < S_k) ? id : -1;
+  };
+
+  // ---- softmax statistics over the valid slots, and the slot count of every
+  //      key range --------------------------------------------------------------
+  const float c2 = P.sm_scale * 1.4426950408889634f;  // base-2 logit scale
+  if (!DENSE) {
+    for (int i = lane; i < NR; i += 64) cursor[i] = 0;
+    wave_lds_sync();
+  }
+  const float2 st = row_softmax_stats(
+      n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of,
+      [&](int key) {
+        if (!DENSE) atomicAdd(&cursor[key / RK], 1);  // counts only: order-free
+      });
+  const float m2 = st.x, invZ = st.y;
+  const float coef = P.grad_loss * P.sm_scale;
+
+  // ---- range table: range i holds [first_i, end_i), then kSinks sink entries
+  //      with key (i+1)*RK; ranges start at multiples of 4 -------------------
+  int2* offrow = reinterpret_cast<int2*>(P.offs) + r * P.NR;
+  int* rkey = P.rkey + r * P.rec_stride;
+  int tail;  // padding lanes store past every range and sink
+  if (DENSE) {
+    // record of slot j at j + kSinks*(j / RK): ranges are already in key order
+    const int nr_used = (n + RK - 1) / RK;
+    tail = n + kSinks * nr_used;
+    if (g == 0) {
+      for (int i = lane; i < NR; i += 64) {
+        const int cnt = n - i * RK < 0 ? 0 : (n - i * RK < RK ? n - i * RK : RK);
+        const int first = i * (RK + kSinks);
+        offrow[i] = cnt > 0 ? make_int2(first, first + cnt) : make_int2(0, 0);
+      }
+      for (int i0 = 0; i0 < nr_used; i0 += 2) {
+        const int i = i0 + half;
+        if (i < nr_used) {
+          const int cnt = n - i * RK < RK ? n - i * RK : RK;
+          rkey[i * (RK + kSinks) + cnt + l32] = (i + 1) * RK;
+        }
+      }
+    }
+  } else {
+    wave_lds_sync();
+    int* ends = reinterpret_cast<int*>(lds);  // scratch until Q' is staged
+    const int per = (NR + 63) / 64;
+    const int s0 = lane * per < NR ? lane * per : NR;
+    const int s1 = s0 + per < NR ? s0 + per : NR;
+    int sum = 0;
+    for (int i = s0; i < s1; ++i) sum += (cursor[i] + kSinks + 3) & ~3;
+    int incl = sum;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - sum;
+    wave_lds_sync();
+    for (int i = s0; i < s1; ++i) {
+      const int cnt = cursor[i];
+      cursor[i] = run;
+      ends[i] = run + cnt;
+      if (g == 0) offrow[i] = make_int2(run, run + cnt);
+      run += (cnt + kSinks + 3) & ~3;
+    }
+    tail = __shfl(incl, 63, 64);
+    wave_lds_sync();
+    if (g == 0) {
+      for (int i0 = 0; i0 < NR; i0 += 2) {
+        const int i = i0 + half;
+        if (i < NR) rkey[ends[i] + l32] = (i + 1) * RK;
+      }
+    }
+    wave_lds_sync();
+  }
+
+  int nbits = 0;
+  while ((1 << nbits) < NR) ++nbits;
+
+  // ---- per-row operands: this wave's heads -----------------------------------
+  const int hl = 32 * g + rotl5(l32);  // head of lane l32 in GEMM1's N dimension
+  const float wv = hl < H ? P.w[r * P.H + hl] : 0.f;
+  // GEMM1 B operand: lane holds q[hl][d = 8*half + 16*kd + e]
+  u32x4_t qb1[KD];
+  const uint16_t* qrow = P.q + r * P.H * D;
+#pragma unroll
+  for (int kd = 0; kd < KD; ++kd)
+    qb1[kd] = hl < H ? *reinterpret_cast<const u32x4_t*>(qrow + hl * D + 8 * half + 16 * kd)
+                     : u32x4_t{0u, 0u, 0u, 0u};
+  // (w*q)^T: Q' rows staged in LDS at the natural head offset rotl5(l32), read
+  // back transposed (lane d = 32*nd + l32, 8 heads from 16*ks + 8*half)
+  {
+    unsigned char* qs = lds;
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) {
+      const u32x4_t v = qb1[kd];
+      u32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf16(wv * bf16_lo(v[e]), wv * bf16_hi(v[e]));
+      *reinterpret_cast<u32x4_t*>(qs + rotl5(l32) * L::kPitch + (8 * half + 16 * kd) * 2) = o;
+    }
+    wave_lds_sync();
+    uint16_t* qtrow = P.qt + r * D * HP + 32 * g;
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) {
+      const int col0 = 32 * nd + 16 * ((lane >> 4) & 1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int r0 = 16 * ks + 8 * half;
+        *reinterpret_cast<u32x4_t*>(qtrow + (32 * nd + l32) * HP + r0) =
+            lds_tr8(qs, L::kPitch, r0, r0 + 4, col0);
+      }
+    }
+    wave_lds_sync();
+  }
+
+  // ---- chunk pipeline ---------------------------------------------------------
+  const int nchunks = (n + kSlots - 1) / kSlots;
+  unsigned char* ktile = lds;
+  auto stage_ptr = [&](int c) -> unsigned char* {
+    return lds + L::kStageOff + (c & 1) * L::kStageBytes;
+  };
+  auto load_raw = [&](int c) -> Raw {
+    const int j = c * kSlots + l32;
+    const int jc = j < row_len ? j : row_len - 1;
+    Raw v;
+    v.id = DENSE ? 0 : idrow[jc];
+    v.I = Irow[jc];
+    v.p = prow[jc];
+    return v;
+  };
+  // dI and key of the lane's slot; lanes l and l+32 publish the same values
+  auto finalize = [&](int c, const Raw& v) -> int {
+    const int j = c * kSlots + l32;
+    const int key = key_of(j, v.id);
+    const float dI = key >= 0 ? slot_dI(v.I, v.p, c2, m2, invZ, coef) : 0.f;
+    reinterpret_cast<float*>(stage_ptr(c))[l32] = dI;
+    reinterpret_cast<int*>(stage_ptr(c) + kSlots * 4)[l32] = key;
+    return key;
+  };
+  // K rows in GEMM1's A layout: lane holds row l32, d = 8*half + 16*kd + e.
+  // Padding slots read row 0; their dI is 0, so they add nothing.
+  auto gather = [&](int key, u32x4_t (&kr)[KD]) {
+    const uint16_t* src = kb + int64_t(key < 0 ? 0 : key) * D + 8 * half;
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) kr[kd] = *reinterpret_cast<const u32x4_t*>(src + 16 * kd);
+  };
+
+  f32x16_t dqacc[ND];
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd) dqacc[nd] = f32x16_t{};
+  float dw_acc = 0.f;
+
+  float* rdi = P.rdi + r * P.rec_stride;
+  uint32_t* rmask = P.rmask + 2 * (r * P.rec_stride);
+
+  u32x4_t kc[KD];
+  Raw raw;
+  if (nchunks > 0) {
+    const int key0 = finalize(0, load_raw(0));
+    gather(key0, kc);
+    raw = load_raw(1);
+  }
+
+  // Records of chunk c are stored in iteration c+1, after the one wait of the
+  // iteration and before its loads: gfx9's vmcnt counts stores too, and a
+  // store issued after a load that is waited for later turns that wait into a
+  // full drain.
+  int prev_pos = tail + l32;
+  int prev_key = -1;
+  float prev_dI = 0.f;
+  uint32_t prev_mask = 0u;
+  for (int c = 0; c < nchunks; ++c) {
+    // ---- GEMM1: S^T[j][h] over d, K_g straight from registers ----------------
+    f32x16_t s = f32x16_t{};
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) s = mfma32(kc[kd], qb1[kd], s);
+
+    // ---- next chunk's slot data; records of the previous chunk ---------------
+    const int key_n = finalize(c + 1, raw);
+    if (g == 0) {
+      rkey[prev_pos] = prev_key;
+      rdi[prev_pos] = prev_dI;
+    }
+    rmask[2 * prev_pos + g] = prev_mask;
+    // K rows of chunk c -> LDS for GEMM2's transposed reads; then chunk c+1's
+    // K rows and chunk c+2's slot data go in flight
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd)
+      *reinterpret_cast<u32x4_t*>(ktile + l32 * L::kPitch + (8 * half + 16 * kd) * 2) = kc[kd];
+    gather(key_n, kc);
+    raw = load_raw(c + 2);
+    wave_lds_sync();
+
+    // ---- G' = dI*[S>0], dW, bf16 packing, sign words --------------------------
+    // lane: head hl; register 4*i + rr <-> slot 8*i + 4*half + rr
+    const float* sd = reinterpret_cast<const float*>(stage_ptr(c));
+    const int* sk = reinterpret_cast<const int*>(stage_ptr(c) + kSlots * 4);
+    float dIv[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(sd + 8 * i + 4 * half);
+      dIv[i][0] = v.x;
+      dIv[i][1] = v.y;
+      dIv[i][2] = v.z;
+      dIv[i][3] = v.w;
+    }
+    uint32_t gp[4][2];
+    uint32_t maskword = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float gv[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float sv = s[4 * i + rr];
+        const bool pos = sv > 0.f;
+        gv[rr] = pos ? dIv[i][rr] : 0.f;
+        dw_acc = fmaf(gv[rr], sv, dw_acc);
+        // low half of the ballot: slot 8*i + rr, high half: slot 8*i + 4 + rr;
+        // lane j of maskword takes the sign word of slot j
+        const uint64_t bal = ballot(pos);
+        maskword = write_lane(maskword, uint32_t(bal), 8 * i + rr);
+        maskword = write_lane(maskword, uint32_t(bal >> 32), 8 * i + 4 + rr);
+      }
+      gp[i][0] = pack_bf16(gv[0], gv[1]);
+      gp[i][1] = pack_bf16(gv[2], gv[3]);
+    }
+
+    // ---- GEMM2: dQ'[h][d] += G'[h][j] K[j][d] ----------------------------------
+    // k-step ks covers slots 16*ks + {0..15}; register e of lane (half) is slot
+    // 16*ks + 8*(e/4) + 4*half + e%4 (GEMM1's output order)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4_t aop = u32x4_t{gp[2 * ks][0], gp[2 * ks][1], gp[2 * ks + 1][0], gp[2 * ks + 1][1]};
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const int col0 = 32 * nd + 16 * ((lane >> 4) & 1);
+        const int r0 = 16 * ks + 4 * half;
+        dqacc[nd] = mfma32(aop, lds_tr8(ktile, L::kPitch, r0, r0 + 8, col0), dqacc[nd]);
+      }
+    }
+
+    // ---- position of every valid slot's record: range start + earlier slots
+    //      of the same range (slot order), identical in both waves of the row --
+    {
+      const int key = sk[l32];
+      const bool valid = lane < kSlots && key >= 0;
+      int pos;
+      if (DENSE) {
+        const int j = c * kSlots + l32;
+        pos = j + kSinks * (j / RK);
+      } else {
+        const int rg = valid ? key / RK : 0;
+        const uint64_t same = same_range_lanes(valid, rg, nbits);
+        const int base = valid ? cursor[rg] : 0;
+        pos = base + __popcll(same & lanemask_lt());
+        wave_lds_sync();
+        if (valid && (same & lanemask_lt()) == 0) cursor[rg] = base + __popcll(same);
+      }
+      // padding lanes and the upper half-wave store into the row's tail
+      prev_pos = valid ? pos : tail + l32;
+      prev_key = key;
+      prev_dI = sd[l32];
+      prev_mask = maskword;
+    }
+    wave_lds_sync();
+  }
+  if (g == 0) {
+    rkey[prev_pos] = prev_key;
+    rdi[prev_pos] = prev_dI;
+  }
+  rmask[2 * prev_pos + g] = prev_mask;
+
+  // ---- row epilogue: dQ = w * dQ', dW -----------------------------------------
+  // dQ' register 4*i + rr of lane (half) is GEMM2's row m = 8*i + 4*half + rr,
+  // i.e. head 32*g + rotl5(m)
+  float* dqrow = P.dq + r * P.H * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int mrow = 8 * i + 4 * half + rr;
+      const int h = 32 * g + rotl5(mrow);
+      const float wh = __shfl(wv, mrow, 64);  // lane mrow holds w of that head
+      if (h < H) {
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) dqrow[h * D + l32 + 32 * nd] = wh * dqacc[nd][4 * i + rr];
+      }
+    }
+  }
+  const float tot = dw_acc + __shfl_xor(dw_acc, 32, 64);
+  if (half == 0 && hl < H) P.dw[r * P.H + hl] = tot;
+}
+
+template <int D, bool DENSE>
+hipError_t launch_t(const Problem& P, hipStream_t stream) {
+  const dim3 grid(unsigned(P.B * P.S_q * (P.HP / 32)));
+  row_export_kernel<D, DENSE><<<grid, 64, 0, stream>>>(P);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const Problem& P, hipStream_t stream) {
+  return P.dense ? launch_t<D, true>(P, stream) : launch_t<D, false>(P, stream);
+}
+
+}  // namespace
+
+hipError_t launch_rows_export(const Problem& P, hipStream_t stream) {
+  switch (P.D) {
+    case 32:
+      return launch_d<32>(P, stream);
+    case 64:
+      return launch_d<64>(P, stream);
+    case 128:
+      return launch_d<128>(P, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ibwd

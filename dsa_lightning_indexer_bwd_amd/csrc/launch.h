@@ -11,6 +11,7 @@ namespace ibwd {
 constexpr int64_t kMaxHeads = 64;
 constexpr int kSlots = 32;          // slots per chunk in the row kernel
 constexpr int kRangeKeys = 256;     // keys per range of the two-pass dK route
+constexpr int kSinks = 32;          // sink entries after every range's records
 constexpr int kMaxRanges = 1024;    // ranges a row can be bucketed into (S_k <= 262144)
 constexpr int kMaxQueryBlock = 1024;  // queries per range-kernel workgroup
 
@@ -19,17 +20,24 @@ enum DkRoute : int {
   kDkAtomic = 1,   // fp32 global atomics straight from the row kernel
 };
 
-// Workspace layout of the two-pass dK route.
-//   rec   [rows][row_len + 32] int4 {key, dI bits, sign bits of h 0..31,
-//         sign bits of h 32..63}: the valid slots of a row grouped by key range
-//         (range r = key / RK), slot order within a range; the last 32 entries
-//         of a row take the row kernel's stores of padding lanes
-//   off   [rows][NR+1]    int: start of each range's records within the row
-//   qt    [rows][D][HP]   bf16: (w*q)^T of every row, heads padded to HP
-//   slab  [B][NQB][NR*RK][D] fp32: per query block partial dK
+// Workspace layout of the two-pass dK route.  A row's valid slots are stored
+// as records grouped by key range (range r = key / RK), slot order within a
+// range.  Range r occupies [first_r, end_r) and is followed by 32 sink
+// entries whose key is (r+1)*RK, one past the range: a 32-slot tile that runs
+// past end_r reads sinks, which the range kernel sends to a scratch row.
+// Every range starts at a multiple of 4 entries.
+//   rkey  [rows][rec_stride] int32  key of the record
+//   rdi   [rows][rec_stride] fp32   dI of the record
+//   rmask [rows][rec_stride][2] u32 sign bits [S > 0] of heads 0..31, 32..63
+//         (bit b of word g is head 32g + rotl5(b), rotl5 = 5-bit rotate left)
+//   offs  [rows][NR] int2           {first, end} record of each range
+//   qt    [rows][D][HP] bf16        (w*q)^T of every row, heads padded to HP
+//   slab  [B][NQB][NR*RK][D] fp32   per query block partial dK
+// rec_stride = row_len + 36*NR (sinks and alignment) + 32 (stores of padding
+// lanes), rounded up to a multiple of 4.
 struct Layout {
   int64_t rows, row_len, rec_stride, HP, RK, NR, NQB, QBS, nchunk;
-  size_t off_rec, off_off, off_qt, off_slab, total;
+  size_t off_rkey, off_rdi, off_rmask, off_offs, off_qt, off_slab, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -39,10 +47,10 @@ inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_
   Layout L{};
   L.rows = B * S_q;
   L.row_len = row_len;
-  L.rec_stride = row_len + kSlots;
   L.HP = H > 32 ? 64 : 32;
   L.RK = kRangeKeys;
   L.NR = (S_k + L.RK - 1) / L.RK;
+  L.rec_stride = (row_len + 36 * L.NR + kSlots + 3) & ~int64_t(3);  // 16-byte aligned rows
   // about 256 range-kernel workgroups (one per CU), at most kMaxQueryBlock
   // queries each
   int64_t nqb = (256 + L.NR * B - 1) / (L.NR * B);
@@ -52,11 +60,16 @@ inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_
   L.QBS = (S_q + nqb - 1) / nqb;
   L.NQB = (S_q + L.QBS - 1) / L.QBS;
   L.nchunk = (row_len + kSlots - 1) / kSlots;
+  const size_t recs = size_t(L.rows) * size_t(L.rec_stride);
   size_t o = 0;
-  L.off_rec = o;
-  o = align256(o + size_t(L.rows) * size_t(L.rec_stride) * 16);
-  L.off_off = o;
-  o = align256(o + size_t(L.rows) * size_t(L.NR + 1) * 4);
+  L.off_rkey = o;
+  o = align256(o + recs * 4);
+  L.off_rdi = o;
+  o = align256(o + recs * 4);
+  L.off_rmask = o;
+  o = align256(o + recs * 8);
+  L.off_offs = o;
+  o = align256(o + size_t(L.rows) * size_t(L.NR) * 8);
   L.off_qt = o;
   o = align256(o + size_t(L.rows) * size_t(D) * size_t(L.HP) * 2);
   L.off_slab = o;
@@ -83,8 +96,10 @@ struct Problem {
   float sm_scale, grad_loss;
   int route;            // DkRoute
   // two-pass exports (carved from the workspace)
-  int4* rec;
-  int* off;
+  int* rkey;
+  float* rdi;
+  uint32_t* rmask;
+  int* offs;  // int2 pairs
   uint16_t* qt;
   float* slab;
   int64_t rec_stride, RK, NR, NQB, QBS, nchunk, HP;
@@ -93,9 +108,12 @@ struct Problem {
 // Enqueue the whole backward on `stream`.  Returns the first HIP error.
 hipError_t launch(Problem P, void* workspace, hipStream_t stream);
 
-// Row kernel (one wave per query row): dQ, dW and either the dK atomics or the
-// two-pass exports.
+// Row kernel of the atomic route (one wave per query row): dQ, dW and the fp32
+// atomic dK scatter.
 hipError_t launch_rows(const Problem& P, hipStream_t stream);
+// Row kernel of the two-pass route (one wave per query row and group of 32
+// heads): dQ, dW, the slot records and (w*q)^T.
+hipError_t launch_rows_export(const Problem& P, hipStream_t stream);
 // Two-pass dK: range-major reduction into per query-block slabs, then the
 // fixed-order sum of the slabs into d_k.
 hipError_t launch_dk(const Problem& P, hipStream_t stream);
