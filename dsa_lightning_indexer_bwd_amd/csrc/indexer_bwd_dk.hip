@@ -189,12 +189,16 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 1) void dk_range_kernel(Proble
     const int64_t ro = int64_t(row) * P.rec_stride;
     const int ia = base + pim;
     tl.w = reinterpret_cast<const uint2*>(P.rmask)[ro + ia];
-    tl.ka = P.rkey[ro + ia];
+    tl.ka = P.rkd[2 * (ro + ia)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ir = base + 16 * half + 4 * i;
-      tl.key[i] = *reinterpret_cast<const int4*>(P.rkey + ro + ir);
-      tl.di[i] = *reinterpret_cast<const float4*>(P.rdi + ro + ir);
+      // {key, dI} of records ir .. ir+3
+      const int4 a = *reinterpret_cast<const int4*>(P.rkd + 2 * (ro + ir));
+      const int4 c = *reinterpret_cast<const int4*>(P.rkd + 2 * (ro + ir) + 4);
+      tl.key[i] = make_int4(a.x, a.z, c.x, c.z);
+      tl.di[i] = make_float4(__int_as_float(a.y), __int_as_float(a.w), __int_as_float(c.y),
+                             __int_as_float(c.w));
     }
     return tl;
   };

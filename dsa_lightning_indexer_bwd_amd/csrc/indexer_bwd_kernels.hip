@@ -40,8 +40,7 @@ hipError_t launch(Problem P, void* workspace, hipStream_t stream) {
     return launch_rows(P, stream);
   }
   char* ws = static_cast<char*>(workspace);
-  P.rkey = reinterpret_cast<int*>(ws + L.off_rkey);
-  P.rdi = reinterpret_cast<float*>(ws + L.off_rdi);
+  P.rkd = reinterpret_cast<int*>(ws + L.off_rkd);
   P.rmask = reinterpret_cast<uint32_t*>(ws + L.off_rmask);
   P.offs = reinterpret_cast<int*>(ws + L.off_offs);
   P.qt = reinterpret_cast<uint16_t*>(ws + L.off_qt);

@@ -41,11 +41,12 @@ namespace {
 template <int D>
 struct ExportLds {
   static constexpr int kPitch = D * 2 + 16;  // bytes per K / Q' row (bank spread)
-  static constexpr int kTile = kSlots * kPitch;  // K chunk; Q' staging (32 rows) aliases it
-  static constexpr int kStageOff = kTile;
+  static constexpr int kTile = kSlots * kPitch;  // one K chunk
+  static constexpr int kStageOff = 2 * kTile;      // two K chunks; Q' staging aliases them
   static constexpr int kStageBytes = kSlots * 8;  // dI (fp32) + key (int32)
-  static constexpr int kCursorOff = kStageOff + 2 * kStageBytes;
-  static constexpr int kBytes = kCursorOff + kMaxRanges * 4;
+  static constexpr int kCursorOff = kStageOff + 4 * kStageBytes;
+  // dynamic size: the cursor holds one int per key range of the problem
+  static size_t bytes(int64_t NR) { return size_t(kCursorOff) + size_t(NR) * 4; }
 };
 
 struct Raw {
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
   constexpr int KD = D / 16;  // GEMM1 k-steps over d
   constexpr int ND = D / 32;  // GEMM2 32-wide d tiles
   using L = ExportLds<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
   const int32_t* idrow = DENSE ? nullptr : P.ids + r * P.row_len;
   const uint16_t* kb = P.k + b * P.S_k * D;
   const int S_k = int(P.S_k);
-  const int RK = int(P.RK);
+  constexpr int RK = kRangeKeys;  // power of two: divisions are shifts
   const int NR = int(P.NR);
   int* cursor = reinterpret_cast<int*>(lds + L::kCursorOff);
 
@@ -126,12 +127,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
   // ---- range table: range i holds [first_i, end_i), then kSinks sink entries
   //      with key (i+1)*RK; ranges start at multiples of 4 -------------------
   int2* offrow = reinterpret_cast<int2*>(P.offs) + r * P.NR;
-  int* rkey = P.rkey + r * P.rec_stride;
-  int tail;  // padding lanes store past every range and sink
+  int2* rkd = reinterpret_cast<int2*>(P.rkd) + r * P.rec_stride;
   if (DENSE) {
     // record of slot j at j + kSinks*(j / RK): ranges are already in key order
     const int nr_used = (n + RK - 1) / RK;
-    tail = n + kSinks * nr_used;
     if (g == 0) {
       for (int i = lane; i < NR; i += 64) {
         const int cnt = n - i * RK < 0 ? 0 : (n - i * RK < RK ? n - i * RK : RK);
@@ -142,7 +141,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
         const int i = i0 + half;
         if (i < nr_used) {
           const int cnt = n - i * RK < RK ? n - i * RK : RK;
-          rkey[i * (RK + kSinks) + cnt + l32] = (i + 1) * RK;
+          rkd[i * (RK + kSinks) + cnt + l32] = make_int2((i + 1) * RK, 0);
         }
       }
     }
@@ -168,12 +167,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
       if (g == 0) offrow[i] = make_int2(run, run + cnt);
       run += (cnt + kSinks + 3) & ~3;
     }
-    tail = __shfl(incl, 63, 64);
     wave_lds_sync();
     if (g == 0) {
       for (int i0 = 0; i0 < NR; i0 += 2) {
         const int i = i0 + half;
-        if (i < NR) rkey[ends[i] + l32] = (i + 1) * RK;
+        if (i < NR) rkd[ends[i] + l32] = make_int2((i + 1) * RK, 0);
       }
     }
     wave_lds_sync();
@@ -220,10 +218,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
   }
 
   // ---- chunk pipeline ---------------------------------------------------------
+  // Iteration c issues GEMM1 of chunk c+1 (K rows already in registers) before
+  // the VALU work of chunk c, so the matrix core and the VALU overlap inside
+  // the wave as well as across the two waves of the SIMD.  Slot data live in
+  // a ring of 4 stages, K rows of chunks c and c+1 in two LDS tiles.
   const int nchunks = (n + kSlots - 1) / kSlots;
-  unsigned char* ktile = lds;
+  auto ktile = [&](int c) -> unsigned char* { return lds + (c & 1) * L::kTile; };
   auto stage_ptr = [&](int c) -> unsigned char* {
-    return lds + L::kStageOff + (c & 1) * L::kStageBytes;
+    return lds + L::kStageOff + (c & 3) * L::kStageBytes;
   };
   auto load_raw = [&](int c) -> Raw {
     const int j = c * kSlots + l32;
@@ -250,51 +252,60 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd) kr[kd] = *reinterpret_cast<const u32x4_t*>(src + 16 * kd);
   };
+  auto store_ktile = [&](int c, const u32x4_t (&kr)[KD]) {
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd)
+      *reinterpret_cast<u32x4_t*>(ktile(c) + l32 * L::kPitch + (8 * half + 16 * kd) * 2) = kr[kd];
+  };
+  auto gemm1 = [&](const u32x4_t (&kr)[KD]) -> f32x16_t {
+    f32x16_t s = f32x16_t{};
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) s = mfma32(kr[kd], qb1[kd], s);
+    return s;
+  };
 
   f32x16_t dqacc[ND];
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) dqacc[nd] = f32x16_t{};
   float dw_acc = 0.f;
 
-  float* rdi = P.rdi + r * P.rec_stride;
   uint32_t* rmask = P.rmask + 2 * (r * P.rec_stride);
 
-  u32x4_t kc[KD];
+  // Records of chunk c are stored in iteration c+1 after the iteration's one
+  // wait and before its loads: gfx9's vmcnt counts stores too, and a store
+  // issued after a load that is waited for later turns that wait into a full
+  // drain.  Only lanes of valid slots store.
+  int prev_pos = 0;
+  bool prev_valid = false;
+  int2 prev_kd = make_int2(-1, 0);
+  uint32_t prev_mask = 0u;
+  auto store_records = [&]() {
+    if (prev_valid) {
+      if (g == 0) rkd[prev_pos] = prev_kd;
+      rmask[2 * prev_pos + g] = prev_mask;
+    }
+  };
+
+  u32x4_t kr[KD];
   Raw raw;
+  f32x16_t sa = f32x16_t{}, sb = f32x16_t{};
   if (nchunks > 0) {
-    const int key0 = finalize(0, load_raw(0));
-    gather(key0, kc);
+    gather(finalize(0, load_raw(0)), kr);
     raw = load_raw(1);
+    sa = gemm1(kr);
+    store_ktile(0, kr);
+    gather(finalize(1, raw), kr);
+    raw = load_raw(2);
   }
 
-  // Records of chunk c are stored in iteration c+1, after the one wait of the
-  // iteration and before its loads: gfx9's vmcnt counts stores too, and a
-  // store issued after a load that is waited for later turns that wait into a
-  // full drain.
-  int prev_pos = tail + l32;
-  int prev_key = -1;
-  float prev_dI = 0.f;
-  uint32_t prev_mask = 0u;
-  for (int c = 0; c < nchunks; ++c) {
-    // ---- GEMM1: S^T[j][h] over d, K_g straight from registers ----------------
-    f32x16_t s = f32x16_t{};
-#pragma unroll
-    for (int kd = 0; kd < KD; ++kd) s = mfma32(kc[kd], qb1[kd], s);
-
-    // ---- next chunk's slot data; records of the previous chunk ---------------
-    const int key_n = finalize(c + 1, raw);
-    if (g == 0) {
-      rkey[prev_pos] = prev_key;
-      rdi[prev_pos] = prev_dI;
-    }
-    rmask[2 * prev_pos + g] = prev_mask;
-    // K rows of chunk c -> LDS for GEMM2's transposed reads; then chunk c+1's
-    // K rows and chunk c+2's slot data go in flight
-#pragma unroll
-    for (int kd = 0; kd < KD; ++kd)
-      *reinterpret_cast<u32x4_t*>(ktile + l32 * L::kPitch + (8 * half + 16 * kd) * 2) = kc[kd];
-    gather(key_n, kc);
-    raw = load_raw(c + 2);
+  // one pipeline step: chunk c with scores s_cur; GEMM1 of chunk c+1 -> s_next
+  auto step = [&](int c, const f32x16_t& s_cur, f32x16_t& s_next) {
+    s_next = gemm1(kr);  // chunk c+1 (padding-only past the end)
+    store_ktile(c + 1, kr);
+    const int key_n2 = finalize(c + 2, raw);
+    store_records();
+    gather(key_n2, kr);
+    raw = load_raw(c + 3);
     wave_lds_sync();
 
     // ---- G' = dI*[S>0], dW, bf16 packing, sign words --------------------------
@@ -317,7 +328,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
       float gv[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const float sv = s[4 * i + rr];
+        const float sv = s_cur[4 * i + rr];
         const bool pos = sv > 0.f;
         gv[rr] = pos ? dIv[i][rr] : 0.f;
         dw_acc = fmaf(gv[rr], sv, dw_acc);
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
       for (int nd = 0; nd < ND; ++nd) {
         const int col0 = 32 * nd + 16 * ((lane >> 4) & 1);
         const int r0 = 16 * ks + 4 * half;
-        dqacc[nd] = mfma32(aop, lds_tr8(ktile, L::kPitch, r0, r0 + 8, col0), dqacc[nd]);
+        dqacc[nd] = mfma32(aop, lds_tr8(ktile(c), L::kPitch, r0, r0 + 8, col0), dqacc[nd]);
       }
     }
 
@@ -362,19 +373,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
         wave_lds_sync();
         if (valid && (same & lanemask_lt()) == 0) cursor[rg] = base + __popcll(same);
       }
-      // padding lanes and the upper half-wave store into the row's tail
-      prev_pos = valid ? pos : tail + l32;
-      prev_key = key;
-      prev_dI = sd[l32];
+      prev_pos = pos;
+      prev_valid = valid;
+      prev_kd = make_int2(key, __float_as_int(sd[l32]));
       prev_mask = maskword;
     }
     wave_lds_sync();
+  };
+  // unrolled by two: the score tiles alternate without register copies
+  for (int c = 0; c < nchunks; c += 2) {
+    step(c, sa, sb);
+    if (c + 1 < nchunks) step(c + 1, sb, sa);
   }
-  if (g == 0) {
-    rkey[prev_pos] = prev_key;
-    rdi[prev_pos] = prev_dI;
-  }
-  rmask[2 * prev_pos + g] = prev_mask;
+  store_records();
 
   // ---- row epilogue: dQ = w * dQ', dW -----------------------------------------
   // dQ' register 4*i + rr of lane (half) is GEMM2's row m = 8*i + 4*half + rr,
@@ -400,7 +411,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
 template <int D, bool DENSE>
 hipError_t launch_t(const Problem& P, hipStream_t stream) {
   const dim3 grid(unsigned(P.B * P.S_q * (P.HP / 32)));
-  row_export_kernel<D, DENSE><<<grid, 64, 0, stream>>>(P);
+  row_export_kernel<D, DENSE><<<grid, 64, ExportLds<D>::bytes(P.NR), stream>>>(P);
   return hipGetLastError();
 }
 

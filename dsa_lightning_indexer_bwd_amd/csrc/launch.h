@@ -26,8 +26,7 @@ enum DkRoute : int {
 // entries whose key is (r+1)*RK, one past the range: a 32-slot tile that runs
 // past end_r reads sinks, which the range kernel sends to a scratch row.
 // Every range starts at a multiple of 4 entries.
-//   rkey  [rows][rec_stride] int32  key of the record
-//   rdi   [rows][rec_stride] fp32   dI of the record
+//   rkd   [rows][rec_stride] int2   {key, dI bits} of the record
 //   rmask [rows][rec_stride][2] u32 sign bits [S > 0] of heads 0..31, 32..63
 //         (bit b of word g is head 32g + rotl5(b), rotl5 = 5-bit rotate left)
 //   offs  [rows][NR] int2           {first, end} record of each range
@@ -37,7 +36,7 @@ enum DkRoute : int {
 // lanes), rounded up to a multiple of 4.
 struct Layout {
   int64_t rows, row_len, rec_stride, HP, RK, NR, NQB, QBS, nchunk;
-  size_t off_rkey, off_rdi, off_rmask, off_offs, off_qt, off_slab, total;
+  size_t off_rkd, off_rmask, off_offs, off_qt, off_slab, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -62,10 +61,8 @@ inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_
   L.nchunk = (row_len + kSlots - 1) / kSlots;
   const size_t recs = size_t(L.rows) * size_t(L.rec_stride);
   size_t o = 0;
-  L.off_rkey = o;
-  o = align256(o + recs * 4);
-  L.off_rdi = o;
-  o = align256(o + recs * 4);
+  L.off_rkd = o;
+  o = align256(o + recs * 8);
   L.off_rmask = o;
   o = align256(o + recs * 8);
   L.off_offs = o;
@@ -96,8 +93,7 @@ struct Problem {
   float sm_scale, grad_loss;
   int route;            // DkRoute
   // two-pass exports (carved from the workspace)
-  int* rkey;
-  float* rdi;
+  int* rkd;  // int2 pairs {key, dI bits}
   uint32_t* rmask;
   int* offs;  // int2 pairs
   uint16_t* qt;
