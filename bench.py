@@ -1,12 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the lightning-indexer backward on one MI355X.
 
-One step = one full backward call (dK fill + main kernel [+ deterministic
-passes]) over the anchor workload B=1, H=64, D=128, S_q=8192, S_k=4096,
-topk=1024 (2% of slots padded), inputs resident in HBM before timing starts.
-Prints ONE JSON line.  Throughput counts 6*H*D*topk FLOP per query (three
-GEMMs of 2*H*D per slot: score recompute, dQ, dK), the count used for the
-pages' own anchor figure.
+One step = one full backward call (row kernel, dK range kernel, slab sum on
+the default route) over the anchor workload B=1, H=64, D=128, S_q=8192,
+S_k=4096, topk=1024 (2% of slots padded), inputs resident in HBM before
+timing starts.  Prints ONE JSON line.  Throughput counts 6*H*D*topk FLOP per
+query (three GEMMs of 2*H*D per slot: score recompute, dQ, dK), the count used
+for the pages' own anchor figure.  Every kernel of the call is also timed with
+HIP events on the kernels' stream (through the library's stage hook); the
+roofline object describes the kernel that takes longest.
 """
 import argparse
 import json
@@ -34,6 +36,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB once (a kernel of "
+                         "known traffic, read by the HBM counter runs to scale them)")
     return ap.parse_args()
 
 
@@ -81,32 +86,75 @@ def main():
             ibwd.indexer_bwd_sparse(q, k, w, ids, I, p, dq, dw, dk,
                                     deterministic=args.deterministic, workspace=ws, stream=stream)
 
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 18  # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
     print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    # events recorded on the stream the kernels run on
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # HIP events recorded on the stream the kernels run on: one pair around
+    # every call, and one after every kernel of the call (the library's stage
+    # hook runs on the host right after each kernel is enqueued)
+    stage_events = []
+
+    def hook(stage, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        stage_events[-1].append((stage, name, e))
+
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(args.steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
+    ibwd.set_stage_hook(hook)
     torch.cuda.synchronize()
     t_all0.record(stream)
-    for e0, e1 in pairs:
+    for e0, e1 in calls:
         e0.record(stream)
+        stage_events.append([])
         step()
         e1.record(stream)
     t_all1.record(stream)
     torch.cuda.synchronize()
-    per_call_ms = [e0.elapsed_time(e1) for e0, e1 in pairs]
+    ibwd.set_stage_hook(None)
+    per_call_ms = [e0.elapsed_time(e1) for e0, e1 in calls]
     total_ms = t_all0.elapsed_time(t_all1)
     med_us = statistics.median(per_call_ms) * 1e3
     mean_us = statistics.fmean(per_call_ms) * 1e3
     flops = wl.flops()
     tflops = flops / (med_us * 1e-6) / 1e12
     ms_per_step = total_ms / args.steps
+
+    # per-kernel durations: event after kernel i minus event after kernel i-1
+    # (the call's first event for i = 0)
+    per_kernel = {}
+    for (e0, _), evs in zip(calls, stage_events):
+        prev = e0
+        for stage, name, e in evs:
+            per_kernel.setdefault((stage, name), []).append(prev.elapsed_time(e) * 1e3)
+            prev = e
+    kernels = []
+    for (stage, name), ts in sorted(per_kernel.items()):
+        bound, work = kernel_model(name, wl, B, H, D, S_q, S_k)
+        mean_k = statistics.fmean(ts)
+        if bound == "mfma":
+            ach, peak, unit = work / (mean_k * 1e-6) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = work / (mean_k * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s"
+        kernels.append({"stage": stage, "kernel": name, "us_mean": round(mean_k, 2),
+                        "us_median": round(statistics.median(ts), 2), "bound": bound,
+                        "algorithmic_work": work, "achieved": round(ach, 3), "peak": peak,
+                        "unit": unit, "frac": round(ach / peak, 4)})
+    dom = max(kernels, key=lambda k: k["us_mean"])
+    traffic = measured_traffic(dom["kernel"], wl.name, bool(args.deterministic))
 
     # algorithmic HBM bytes of one call (inputs read once, outputs written once)
     row = wl.S_k if wl.dense else wl.topk
@@ -138,24 +186,81 @@ def main():
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "flop_per_call": flops,
         "roofline": {
-            "bound": "mfma",
-            "achieved": round(tflops, 3),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
-            "kernel": "full call (dK fill + main kernel), median of per-call HIP events on the "
-                      "kernels' stream",
-            "hbm_algorithmic_bytes": hbm_bytes,
-            "hbm_GBs_at_this_time": round(hbm_bytes / (med_us * 1e-6) / 1e9, 1),
+            "bound": dom["bound"],
+            "achieved": dom["achieved"],
+            "peak": dom["peak"],
+            "unit": dom["unit"],
+            "frac": dom["frac"],
+            "traffic": traffic,
+            "kernel": dom["kernel"],
+            "us_mean": dom["us_mean"],
+            "algorithmic_work": dom["algorithmic_work"],
         },
+        "kernels": kernels,
+        "call_hbm_algorithmic_bytes": hbm_bytes,
         "pages_context": {"kernel_gemm_us_B200_anchor": 1688.8,
-                          "note": "NVIDIA B200 kernel-2-only figure from the pages; context only"},
+                          "note": "NVIDIA B200 figure from the pages; context only"},
     }
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def kernel_model(name, wl, B, H, D, S_q, S_k):
+    """(bound, algorithmic work per launch) of one kernel of the call.
+
+    Work units per query row are the row's slots (topk, or t+1 for the dense
+    variant): the row kernels do GEMM1 + GEMM2 (4*H*D FLOP per slot), the range
+    kernel the dK GEMM (2*H*D per slot), the atomic-route row kernel all three.
+    The slab sum reads every query block's partial dK once and writes d_k."""
+    slots = wl.flops() // (6 * H * D)
+    if name == "row_export_kernel":
+        return "mfma", 4 * H * D * slots
+    if name == "dk_range_kernel":
+        return "mfma", 2 * H * D * slots
+    if name == "row_kernel":
+        return "mfma", 6 * H * D * slots
+    if name == "dk_sum_kernel":
+        nr = (S_k + 255) // 256
+        nqb = max(-(-256 // (nr * B)), -(-S_q // 1024))
+        nqb = max(1, min(nqb, S_q))
+        qbs = -(-S_q // nqb)
+        nqb = -(-S_q // qbs)
+        return "hbm", (nqb + 1) * B * S_k * D * 4
+    if name == "zero_u32_kernel":
+        return "hbm", B * S_k * D * 4
+    raise KeyError(name)
+
+
+def source_digest():
+    """sha256 over the HIP library sources (the key of a stored counter run)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dsa_lightning_indexer_bwd_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, deterministic):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known size),
+    or None when there is none for this kernel and workload or the library
+    sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    want = source_digest()
+    for line in open(path):
+        if not line.startswith("traffic:"):
+            continue
+        kv = dict(t.split("=", 1) for t in line.split()[1:])
+        if kv.get("kernel") == kernel and kv.get("src") == want:
+            return int(float(kv["fetch_bytes"]) + float(kv["write_bytes"]))
+    return None
 
 
 def cpu_baseline(x, wl, target_s):

@@ -17,6 +17,7 @@ __all__ = [
     "indexer_bwd_dense",
     "indexer_bwd_workspace_bytes",
     "indexer_bwd_strerror",
+    "set_stage_hook",
     "library",
     "IBWD_OK",
     "IBWD_ERR_INVALID_ARGUMENT",
@@ -36,6 +37,8 @@ IBWD_FLAG_ATOMIC_DK = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_indexer_bwd.so")
 _lib = None
+_HOOK_T = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p)
+_hook_ref = None  # keeps the ctypes callback alive while it is installed
 
 
 class IndexerBwdError(RuntimeError):
@@ -64,8 +67,23 @@ def library() -> ctypes.CDLL:
         lib.indexer_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.indexer_bwd_strerror.argtypes = [ctypes.c_int]
         lib.indexer_bwd_strerror.restype = ctypes.c_char_p
+        lib.indexer_bwd_set_stage_hook.argtypes = [_HOOK_T, ctypes.c_void_p]
+        lib.indexer_bwd_set_stage_hook.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def set_stage_hook(fn) -> None:
+    """Profiling aid: fn(stage, kernel_name) runs on the host right after each
+    kernel of a call is enqueued (see indexer_bwd_set_stage_hook); None removes it."""
+    global _hook_ref
+    if fn is None:
+        library().indexer_bwd_set_stage_hook(_HOOK_T(), None)
+        _hook_ref = None
+        return
+    cb = _HOOK_T(lambda user, stage, name: fn(int(stage), name.decode()))
+    library().indexer_bwd_set_stage_hook(cb, None)
+    _hook_ref = cb
 
 
 def indexer_bwd_strerror(status: int) -> str:

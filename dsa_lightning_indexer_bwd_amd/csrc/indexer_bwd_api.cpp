@@ -175,4 +175,9 @@ const char* indexer_bwd_strerror(int status) {
   }
 }
 
+int indexer_bwd_set_stage_hook(indexer_bwd_stage_hook_t hook, void* user) {
+  ibwd::set_stage_hook(hook, user);
+  return IBWD_OK;
+}
+
 }  // extern "C"

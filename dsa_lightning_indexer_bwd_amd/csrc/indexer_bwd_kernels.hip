@@ -21,7 +21,19 @@ __global__ void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
 }
 
+StageHook g_hook = nullptr;
+void* g_hook_user = nullptr;
+
 }  // namespace
+
+void set_stage_hook(StageHook hook, void* user) {
+  g_hook = hook;
+  g_hook_user = user;
+}
+
+void stage_done(int stage, const char* kernel) {
+  if (g_hook) g_hook(g_hook_user, stage, kernel);
+}
 
 hipError_t launch(Problem P, void* workspace, hipStream_t stream) {
   hipError_t err;
@@ -37,7 +49,10 @@ hipError_t launch(Problem P, void* workspace, hipStream_t stream) {
     const int64_t n = P.B * P.S_k * P.D;
     zero_u32_kernel<<<1024, 256, 0, stream>>>(reinterpret_cast<uint32_t*>(P.dk), n);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    return launch_rows(P, stream);
+    stage_done(0, "zero_u32_kernel");
+    if ((err = launch_rows(P, stream)) != hipSuccess) return err;
+    stage_done(1, "row_kernel");
+    return hipSuccess;
   }
   char* ws = static_cast<char*>(workspace);
   P.rkd = reinterpret_cast<int*>(ws + L.off_rkd);
@@ -46,7 +61,8 @@ hipError_t launch(Problem P, void* workspace, hipStream_t stream) {
   P.qt = reinterpret_cast<uint16_t*>(ws + L.off_qt);
   P.slab = reinterpret_cast<float*>(ws + L.off_slab);
   if ((err = launch_rows_export(P, stream)) != hipSuccess) return err;
-  return launch_dk(P, stream);
+  stage_done(0, "row_export_kernel");
+  return launch_dk(P, stream);  // reports stages 1 and 2
 }
 
 }  // namespace ibwd

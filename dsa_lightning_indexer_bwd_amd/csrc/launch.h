@@ -101,6 +101,12 @@ struct Problem {
   int64_t rec_stride, RK, NR, NQB, QBS, nchunk, HP;
 };
 
+// Profiling hook of the C ABI (indexer_bwd_set_stage_hook); the launch code
+// reports every enqueued kernel through stage_done.
+typedef void (*StageHook)(void* user, int stage, const char* kernel);
+void set_stage_hook(StageHook hook, void* user);
+void stage_done(int stage, const char* kernel);
+
 // Enqueue the whole backward on `stream`.  Returns the first HIP error.
 hipError_t launch(Problem P, void* workspace, hipStream_t stream);
 

@@ -31,7 +31,8 @@
  *     Duplicate ids are independent slots.
  *   - Ownership: the caller owns every buffer.  The library allocates nothing,
  *     frees nothing, keeps no state between calls apart from a per-device cache
- *     of the device check, never synchronises, and only enqueues work on
+ *     of the device check (and the optional profiling hook below), never
+ *     synchronises, and only enqueues work on
  *     `stream` (0 = the null stream).  Inputs are read-only (attn_score too).
  *     d_q, d_w and d_k are overwritten in full (d_k is zeroed by the library).
  *   - Alignment: q, k, d_q, d_k must be 16-byte aligned; w, index_score,
@@ -119,10 +120,11 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
 /*
  * indexer_bwd_workspace_bytes — device scratch needed by a call with these
  * arguments (dense != 0 selects indexer_bwd_dense; topk is ignored then).
- * The default route needs 16 bytes per slot (plus 512 per row), (w*q)^T in
- * bf16 (2*H_pad*D bytes per row, H_pad = 32 or 64) and the per query-block dK
- * partial sums (about 320 MB in all at B=1, S_q=8192, S_k=4096, H=64, D=128,
- * topk=1024); IBWD_FLAG_ATOMIC_DK needs none (0).
+ * The default route needs 16 bytes per record entry (topk + 36 per 256-key
+ * range + 32 entries per row), 8 bytes per row and key range for the range
+ * table, (w*q)^T in bf16 (2*H_pad*D bytes per row, H_pad = 32 or 64) and the
+ * per query-block dK partial sums (about 370 MB in all at B=1, S_q=8192,
+ * S_k=4096, H=64, D=128, topk=1024); IBWD_FLAG_ATOMIC_DK needs none (0).
  * Returns 0 for invalid shapes as well; the call itself reports those.
  */
 size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_k, int64_t H,
@@ -130,6 +132,20 @@ size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_
 
 /* indexer_bwd_strerror — static text for a status code (never NULL). */
 const char* indexer_bwd_strerror(int status);
+
+/*
+ * indexer_bwd_set_stage_hook — profiling aid, outside the numerical contract.
+ * While a hook is set, every call of indexer_bwd_sparse / indexer_bwd_dense
+ * calls hook(user, stage, kernel) on the host right after it has enqueued its
+ * kernel number `stage` (0, 1, ...) on the call's stream; `kernel` is a static
+ * name.  A hook that records a HIP event on that stream therefore separates
+ * the kernels of a call in stream order, which lets a caller time each kernel
+ * with events.  The hook must not enqueue work that changes the call's
+ * buffers.  The setting is process-wide and not synchronised: set it while no
+ * other thread calls the library.  hook = NULL removes it.  Returns IBWD_OK.
+ */
+typedef void (*indexer_bwd_stage_hook_t)(void* user, int stage, const char* kernel);
+int indexer_bwd_set_stage_hook(indexer_bwd_stage_hook_t hook, void* user);
 
 #ifdef __cplusplus
 }

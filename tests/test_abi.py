@@ -98,3 +98,18 @@ def test_valid_arguments_without_gpu_fail_cleanly():
         pytest.skip("a GPU is present: covered by the GPU tests")
     for a in (sparse_args(), sparse_args(flags=ibwd.IBWD_FLAG_ATOMIC_DK, ws=None, ws_bytes=0)):
         assert call_sparse(a) in (ibwd.IBWD_ERR_HIP, ibwd.IBWD_ERR_UNSUPPORTED_DEVICE)
+
+
+def test_stage_hook_set_and_remove_without_gpu():
+    """The profiling hook installs and uninstalls; a call rejected before launch
+    (invalid arguments) reports no kernel to it."""
+    seen = []
+    ibwd.set_stage_hook(lambda stage, name: seen.append((stage, name)))
+    try:
+        lib = ibwd.library()
+        st = lib.indexer_bwd_sparse(*([None] * 9), 1, 4, 16, 4, 32, 4, 1.0, 1.0, 0, None, 0, None)
+        assert st == ibwd.IBWD_ERR_INVALID_ARGUMENT
+    finally:
+        ibwd.set_stage_hook(None)
+    assert seen == []
+    assert ibwd.library().indexer_bwd_set_stage_hook(ibwd._HOOK_T(), None) == ibwd.IBWD_OK

@@ -258,3 +258,22 @@ def test_full_size_workload(ibwd, name):
     lhs = np.einsum("bthd,bthd->bth", q, got[0].astype(np.float64))
     rhs = x.w.astype(np.float64) * got[1].astype(np.float64)
     assert relrms(lhs, rhs) < 2e-2, relrms(lhs, rhs)
+
+
+def test_stage_hook_reports_every_kernel(ibwd):
+    """The profiling hook runs once per enqueued kernel, in launch order, on both routes."""
+    log("case: stage hook")
+    x = make_inputs("tiny", seed=3)
+    seen = []
+    ibwd.set_stage_hook(lambda stage, name: seen.append((stage, name)))
+    try:
+        a = run(ibwd, x)
+        b = run(ibwd, x, atomic_dk=True)
+    finally:
+        ibwd.set_stage_hook(None)
+    assert seen == [(0, "row_export_kernel"), (1, "dk_range_kernel"), (2, "dk_sum_kernel"),
+                    (0, "zero_u32_kernel"), (1, "row_kernel")]
+    c = run(ibwd, x)  # hook removed: nothing more is reported
+    assert len(seen) == 5
+    assert all(np.array_equal(u, v) for u, v in zip(a, c))
+    assert_parity("hook-atomic", b, oracle.Problem.from_inputs(x).backward())
