@@ -27,7 +27,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle with gcc (OpenMP).  Returns the library path."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O3", "-march=native", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+        cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
                "-o", tmp, _SRC, "-lm"]
         subprocess.check_call(cmd)
         os.replace(tmp, _LIB_PATH)
