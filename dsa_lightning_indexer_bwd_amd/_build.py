@@ -16,6 +16,9 @@ HOST_SOURCES = ["indexer_bwd_api.cpp"]
 # Device code: gfx950 only; packed-fp32 VALU forms disabled (they are formed
 # by the compiler from ordinary float code otherwise).
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The range kernel's MFMA accumulators are consumed by VALU right away: keep
+# them in VGPRs (the default AGPR form costs a copy per accumulator register).
+PER_FILE_FLAGS = {"indexer_bwd_dk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 
@@ -30,7 +33,8 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        cmd = [hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS
+        cmd = ([hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS
+               + PER_FILE_FLAGS.get(src, []))
         _run(cmd, verbose)
         objs.append(obj)
     for src in HOST_SOURCES:

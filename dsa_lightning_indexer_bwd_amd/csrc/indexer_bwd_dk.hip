@@ -50,7 +50,9 @@ struct DkShape {
   static constexpr int RK = kRangeKeys;
   static constexpr int kSlabBytes = (RK + 1) * D * 4;  // row RK: sink of empty tile rows
   static constexpr int kStampOff = kSlabBytes;
-  static constexpr int kListOff = kStampOff + NW * RK * 4;
+  static constexpr int kStampStride = RK + 4;  // per wave; entry RK takes inactive lanes
+  static constexpr int kStageOff = kStampOff + NW * kStampStride * 4;  // per wave: 32 int2
+  static constexpr int kListOff = kStageOff + NW * kTile * 8;
   static constexpr int kBytes = kListOff + kMaxQueryBlock * 16;
   static_assert(kSlabBytes >= kMaxQueryBlock * 4, "slab doubles as scan scratch");
 };
@@ -79,18 +81,20 @@ __device__ int wave_exclusive_scan(int* a, int n) {
   return __shfl(incl, 63, 64);
 }
 
-// Records of one 32-slot tile as the lane needs them.  MFMA row m (the A
-// operand's lane m = l32) takes record base + pi(m), pi(8i + 4h + r) =
-// 16h + 4i + r, so that accumulator register 4i + r of a lane in half h is the
-// record base + 16h + 4i + r: four aligned 16-byte loads give a lane the keys
-// (and four the dI) of its 16 rows.
+// Records of one 32-slot tile.  MFMA row m (the A operand's lane m = l32)
+// takes record base + pi(m), pi(8i + 4h + r) = 16h + 4i + r, so that
+// accumulator register 4i + r of a lane in half h is the record
+// base + 16h + 4i + r.  A lane loads only the record of its MFMA row (lanes l
+// and l+32 the same one); the keys and dI of its 16 accumulator rows come
+// from a per-wave LDS stage, where the 32 records of the tile are four
+// 16-byte broadcast reads per half-wave away.  (Loading them from global
+// memory per lane would move 16 times the tile's bytes through the vector
+// memory path.)
 // Entries past a range's end are sinks (key one past the range), so a tile
 // needs no bounds checks: sink rows land in the slab's scratch row RK.
 struct Tile {
-  uint2 w;      // sign words of record base + pi(l32)
-  int ka;       // key of record base + pi(l32)
-  int4 key[4];  // keys of records base + 16*half + 4*i + (0..3)
-  float4 di[4];  // their dI
+  uint2 w;   // sign words of record base + pi(l32)
+  int2 kd;   // {key, dI bits} of record base + pi(l32)
 };
 
 template <int NH, int D>
@@ -161,8 +165,8 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 1) void dk_range_kernel(Proble
   const int nne = nne_s;
 
   for (int i = tid; i < (RK + 1) * D; i += NTH) slab[i] = 0.f;
-  int* stamp = reinterpret_cast<int*>(lds + S::kStampOff) + wv * RK;
-  for (int i = lane; i < RK; i += 64) stamp[i] = 0;
+  int* stamp = reinterpret_cast<int*>(lds + S::kStampOff) + wv * S::kStampStride;
+  for (int i = lane; i < S::kStampStride; i += 64) stamp[i] = 0;
   __syncthreads();
 
   const int col = 32 * wv + l32;  // the lane's slab column
@@ -177,40 +181,55 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 1) void dk_range_kernel(Proble
   const int pim = 16 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
 
   // B operand: (w*q)^T, lane holds d = col, h = 16*ks + 8*half + e
+  // Query-level values (list entries) are wave-uniform: moving them to scalar
+  // registers makes every record and (w*q)^T address a scalar row base plus a
+  // 32-bit per-lane offset.
+  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  const uint32_t qt_lane = uint32_t((col * HP + 8 * half) * 2);
   auto load_qt = [&](int row, u32x4_t (&a)[KS]) {
-    const uint16_t* qtrow = P.qt + int64_t(row) * D * HP + col * HP + 8 * half;
+    const char* qtrow = reinterpret_cast<const char*>(P.qt) + size_t(uni(row)) * (D * HP * 2);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const u32x4_t*>(qtrow + 16 * ks);
+    for (int ks = 0; ks < KS; ++ks)
+      a[ks] = *reinterpret_cast<const u32x4_t*>(qtrow + qt_lane + 32 * ks);
   };
   // records of the tile starting at `base` (at most 31 entries past the
   // range's end: inside its sink entries)
   auto load_tile = [&](int row, int base) -> Tile {
     Tile tl;
-    const int64_t ro = int64_t(row) * P.rec_stride;
-    const int ia = base + pim;
-    tl.w = reinterpret_cast<const uint2*>(P.rmask)[ro + ia];
-    tl.ka = P.rkd[2 * (ro + ia)];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ir = base + 16 * half + 4 * i;
-      // {key, dI} of records ir .. ir+3
-      const int4 a = *reinterpret_cast<const int4*>(P.rkd + 2 * (ro + ir));
-      const int4 c = *reinterpret_cast<const int4*>(P.rkd + 2 * (ro + ir) + 4);
-      tl.key[i] = make_int4(a.x, a.z, c.x, c.z);
-      tl.di[i] = make_float4(__int_as_float(a.y), __int_as_float(a.w), __int_as_float(c.y),
-                             __int_as_float(c.w));
-    }
+    const size_t rb = size_t(uni(row)) * size_t(P.rec_stride) * 8;
+    const uint32_t ia = uint32_t(uni(base) + pim) * 8;
+    tl.w = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(P.rmask) + rb + ia);
+    tl.kd = *reinterpret_cast<const int2*>(reinterpret_cast<const char*>(P.rkd) + rb + ia);
     return tl;
   };
+  int2* stage = reinterpret_cast<int2*>(lds + S::kStageOff) + wv * kTile;
 
-  int tile_id = 0;
   // one tile of records tl with B operand qa
   auto process = [&](const Tile& tl, const u32x4_t (&qa)[KS]) {
-    // are the tile's keys pairwise distinct?  (stamps are per wave; sinks,
-    // key - R0 == RK, are not counted)
-    ++tile_id;
-    bool clash = false;
-    if (half == 0 && tl.ka - R0 < RK) clash = atomicExch(&stamp[tl.ka - R0], tile_id) == tile_id;
+    // are the tile's keys pairwise distinct?  Each lane of the lower half
+    // writes its lane number at its key's stamp and reads it back (one wave's
+    // LDS accesses run in order): lanes that share a key read the one lane
+    // number that won, so all but one of them see a clash.  Lanes of the upper
+    // half and sinks (key - R0 == RK) use the spare entry RK and do not count.
+    // Stamps are per wave.
+    const int ka = tl.kd.x;
+    const bool active = half == 0 && ka - R0 < RK;
+    int* sp = &stamp[active ? ka - R0 : RK];
+    *sp = lane;
+    if (half == 0) stage[pim] = tl.kd;
+    wave_lds_sync();
+    const int stamp_old = *sp;
+    // keys and dI of the lane's accumulator rows base + 16*half + 4i + (0..3)
+    int4 key[4];
+    float4 di[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int4 a = *reinterpret_cast<const int4*>(stage + 16 * half + 4 * i);
+      const int4 c = *reinterpret_cast<const int4*>(stage + 16 * half + 4 * i + 2);
+      key[i] = make_int4(a.x, a.z, c.x, c.z);
+      di[i] = make_float4(__int_as_float(a.y), __int_as_float(a.w), __int_as_float(c.y),
+                          __int_as_float(c.w));
+    }
 
     f32x16_t acc = f32x16_t{};
 #pragma unroll
@@ -222,30 +241,32 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 1) void dk_range_kernel(Proble
       acc = mfma32(av, qa[ks], acc);
     }
 
-    // accumulator register 4i + r: record base + 16*half + 4i + r, column col
-    const int cbase = col - R0 * D;
+    // accumulator register 4i + r: record base + 16*half + 4i + r, column col;
+    // byte offsets into the slab (the sink key R0 + RK lands on row RK)
+    const int cbase = (col - R0 * D) * 4;
     int addr[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      addr[4 * i + 0] = tl.key[i].x * D + cbase;
-      addr[4 * i + 1] = tl.key[i].y * D + cbase;
-      addr[4 * i + 2] = tl.key[i].z * D + cbase;
-      addr[4 * i + 3] = tl.key[i].w * D + cbase;
+      addr[4 * i + 0] = key[i].x * (D * 4) + cbase;
+      addr[4 * i + 1] = key[i].y * (D * 4) + cbase;
+      addr[4 * i + 2] = key[i].z * (D * 4) + cbase;
+      addr[4 * i + 3] = key[i].w * (D * 4) + cbase;
     }
-    const float dv[16] = {tl.di[0].x, tl.di[0].y, tl.di[0].z, tl.di[0].w, tl.di[1].x, tl.di[1].y,
-                          tl.di[1].z, tl.di[1].w, tl.di[2].x, tl.di[2].y, tl.di[2].z, tl.di[2].w,
-                          tl.di[3].x, tl.di[3].y, tl.di[3].z, tl.di[3].w};
+    auto at = [&](int k) -> float& { return *reinterpret_cast<float*>(lds + addr[k]); };
+    const float dv[16] = {di[0].x, di[0].y, di[0].z, di[0].w, di[1].x, di[1].y, di[1].z, di[1].w,
+                          di[2].x, di[2].y, di[2].z, di[2].w, di[3].x, di[3].y, di[3].z, di[3].w};
+    const bool clash = active && stamp_old != lane;
     if (ballot(clash) == 0) {
       float old[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) old[k] = slab[addr[k]];
+      for (int k = 0; k < 16; ++k) old[k] = at(k);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) slab[addr[k]] = fmaf(dv[k], acc[k], old[k]);
+      for (int k = 0; k < 16; ++k) at(k) = fmaf(dv[k], acc[k], old[k]);
     } else {
       // ordered path: one slab row (one register of one half-wave) at a time
       for (int k = 0; k < 16; ++k) {
         for (int hh = 0; hh < 2; ++hh) {
-          if (half == hh) slab[addr[k]] = fmaf(dv[k], acc[k], slab[addr[k]]);
+          if (half == hh) at(k) = fmaf(dv[k], acc[k], at(k));
           wave_lds_sync();
         }
       }
