@@ -98,7 +98,7 @@ struct Tile {
 };
 
 template <int NH, int D>
-__global__ __launch_bounds__(64 * DkShape<D>::NW, 1) void dk_range_kernel(Problem P) {
+__global__ __launch_bounds__(64 * DkShape<D>::NW, 2) void dk_range_kernel(Problem P) {
   using S = DkShape<D>;
   constexpr int KS = NH * 2;  // 16-deep k-steps over the heads
   constexpr int HP = NH * 32;
@@ -275,7 +275,10 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 1) void dk_range_kernel(Proble
   // all tiles of one query; f is its first tile, loaded a query earlier.
   // Tiles are prefetched one ahead with the loop unrolled by two so that no
   // loaded register is copied (a copy would wait for the load).
-  auto run_query = [&](const int4& e, const u32x4_t (&qa)[KS], const Tile& f) {
+  auto run_query = [&](const int4 el, const u32x4_t (&qa)[KS], const Tile& f) {
+    // the entry in scalar registers: no LDS read (and no wait behind the
+    // previous tile's slab writes) inside the tile loop
+    const int4 e = make_int4(uni(el.x), uni(el.y), uni(el.z), 0);
     const int ntl = (e.z - e.y + kTile - 1) / kTile;
     const int last = e.y + kTile * (ntl - 1);
     auto tbase = [&](int tt) { return e.y + kTile * tt < last ? e.y + kTile * tt : last; };

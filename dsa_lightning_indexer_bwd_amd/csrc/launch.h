@@ -10,10 +10,10 @@ namespace ibwd {
 
 constexpr int64_t kMaxHeads = 64;
 constexpr int kSlots = 32;          // slots per chunk in the row kernel
-constexpr int kRangeKeys = 256;     // keys per range of the two-pass dK route
+constexpr int kRangeKeys = 128;     // keys per range of the two-pass dK route
 constexpr int kSinks = 32;          // sink entries after every range's records
-constexpr int kMaxRanges = 1024;    // ranges a row can be bucketed into (S_k <= 262144)
-constexpr int kMaxQueryBlock = 1024;  // queries per range-kernel workgroup
+constexpr int kMaxRanges = 2048;    // ranges a row can be bucketed into (S_k <= 262144)
+constexpr int kMaxQueryBlock = 512;  // queries per range-kernel workgroup
 
 enum DkRoute : int {
   kDkTwoPass = 0,  // masks + records exported, range-major LDS reduction (deterministic)
@@ -50,9 +50,9 @@ inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_
   L.RK = kRangeKeys;
   L.NR = (S_k + L.RK - 1) / L.RK;
   L.rec_stride = (row_len + 36 * L.NR + kSlots + 3) & ~int64_t(3);  // 16-byte aligned rows
-  // about 256 range-kernel workgroups (one per CU), at most kMaxQueryBlock
+  // about 512 range-kernel workgroups (two per CU), at most kMaxQueryBlock
   // queries each
-  int64_t nqb = (256 + L.NR * B - 1) / (L.NR * B);
+  int64_t nqb = (512 + L.NR * B - 1) / (L.NR * B);
   if (nqb < (S_q + kMaxQueryBlock - 1) / kMaxQueryBlock) nqb = (S_q + kMaxQueryBlock - 1) / kMaxQueryBlock;
   if (nqb > S_q) nqb = S_q;
   if (nqb < 1) nqb = 1;
