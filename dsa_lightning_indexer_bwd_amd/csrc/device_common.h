@@ -97,17 +97,20 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_bal
 
 // Softmax statistics of one query row over its valid slots, in base 2: with
 // c2 = sm_scale*log2(e), m2 = max_j c2*I_j and invZ = 1 / sum_j 2^(c2*I_j - m2)
-// over the slots j < n whose key_of(j, id_at(j)) >= 0; on_valid(key) is called
-// once per valid slot.  c2*I is rounded before m2 is subtracted (no
-// contraction into a multiply-add), so the largest logit gets 2^0 = 1 exactly.
+// over the slots j < n whose key_of(j, id_at(j)) >= 0.  One pass: each lane
+// keeps a running max and a sum rescaled to it, then the wave combines them.
+// c2*I is rounded before any max is subtracted (no contraction into a
+// multiply-add), so the largest logit contributes 2^0 = 1 exactly.
+// on_group(key) is called by every lane, in uniform control flow, once per
+// slot position j0 + 64u + lane (key < 0 for padding and positions past n).
 // Both row kernels use this and slot_dI, so their dI agree bit for bit.
-template <typename IdAt, typename KeyOf, typename OnValid>
+template <typename IdAt, typename KeyOf, typename OnGroup>
 __device__ __forceinline__ float2 row_softmax_stats(int n, const float* __restrict__ Irow, float c2,
-                                                    IdAt id_at, KeyOf key_of, OnValid on_valid) {
+                                                    IdAt id_at, KeyOf key_of, OnGroup on_group) {
 #pragma clang fp contract(off)
   constexpr int kU = 8;  // loads in flight per lane
   const int lane = threadIdx.x & 63;
-  float m2 = -INFINITY;
+  float m2 = -INFINITY, z = 0.f;
   for (int j0 = 0; j0 < n; j0 += 64 * kU) {
     int idv[kU];
     float iv[kU];
@@ -122,31 +125,18 @@ __device__ __forceinline__ float2 row_softmax_stats(int n, const float* __restri
     for (int u = 0; u < kU; ++u) {
       const int key = key_of(j0 + 64 * u + lane, idv[u]);
       if (key >= 0) {
-        m2 = fmaxf(m2, c2 * iv[u]);
-        on_valid(key);
+        const float v = c2 * iv[u];
+        const float mn = fmaxf(m2, v);
+        z = z * __builtin_amdgcn_exp2f(m2 - mn) + __builtin_amdgcn_exp2f(v - mn);
+        m2 = mn;
       }
+      if (j0 + 64 * u < n) on_group(key);
     }
   }
-  m2 = wave_max(m2);
-  float z = 0.f;
-  for (int j0 = 0; j0 < n; j0 += 64 * kU) {
-    int idv[kU];
-    float iv[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int j = j0 + 64 * u + lane;
-      const int jc = j < n ? j : n - 1;
-      idv[u] = id_at(jc);
-      iv[u] = Irow[jc];
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const float e = __builtin_amdgcn_exp2f(c2 * iv[u] - m2);
-      z += key_of(j0 + 64 * u + lane, idv[u]) >= 0 ? e : 0.f;
-    }
-  }
+  const float mw = wave_max(m2);
+  z = m2 > -INFINITY ? z * __builtin_amdgcn_exp2f(m2 - mw) : 0.f;
   z = wave_sum(z);
-  return make_float2(m2, z > 0.f ? 1.f / z : 0.f);
+  return make_float2(mw, z > 0.f ? 1.f / z : 0.f);
 }
 
 // dI of one valid slot: coef * (softmax - p), coef = grad_loss * sm_scale.

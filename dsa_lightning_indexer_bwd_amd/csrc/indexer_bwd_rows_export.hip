@@ -116,10 +116,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
     for (int i = lane; i < NR; i += 64) cursor[i] = 0;
     wave_lds_sync();
   }
+  int nbits = 0;
+  while ((1 << nbits) < NR) ++nbits;
+  // range counts without LDS atomics (gfx950 runs those at about 190 cycles
+  // per instruction for the whole CU): the lowest lane of every group of
+  // lanes with the same range adds the group's size; leaders have distinct
+  // ranges, so their plain read-modify-writes never collide
   const float2 st = row_softmax_stats(
-      n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of,
-      [&](int key) {
-        if (!DENSE) atomicAdd(&cursor[key / RK], 1);  // counts only: order-free
+      n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [&](int key) {
+        if (!DENSE) {
+          const bool valid = key >= 0;
+          const int rg = valid ? key / RK : 0;
+          const uint64_t same = same_range_lanes(valid, rg, nbits);
+          if (valid && (same & lanemask_lt()) == 0) cursor[rg] += __popcll(same);
+          wave_lds_sync();
+        }
       });
   const float m2 = st.x, invZ = st.y;
   const float coef = P.grad_loss * P.sm_scale;
@@ -176,9 +187,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
     }
     wave_lds_sync();
   }
-
-  int nbits = 0;
-  while ((1 << nbits) < NR) ++nbits;
 
   // ---- per-row operands: this wave's heads -----------------------------------
   const int hl = 32 * g + rotl5(l32);  // head of lane l32 in GEMM1's N dimension
