@@ -222,8 +222,10 @@ def kernel_model(name, wl, B, H, D, S_q, S_k):
     if name == "row_kernel":
         return "mfma", 6 * H * D * slots
     if name == "dk_sum_kernel":
-        nr = (S_k + 255) // 256
-        nqb = max(-(-256 // (nr * B)), -(-S_q // 1024))
+        # query blocks as the library lays them out: 128-key ranges, about
+        # 512 range workgroups, at most 512 queries per block
+        nr = (S_k + 127) // 128
+        nqb = max(-(-512 // (nr * B)), -(-S_q // 512))
         nqb = max(1, min(nqb, S_q))
         qbs = -(-S_q // nqb)
         nqb = -(-S_q // qbs)

@@ -12,12 +12,15 @@
 // {key, dI, the sign bits [S[h,j] > 0] of every h} grouped by key range, and
 // (w*q)^T of the row.
 //
-// Splitting the 64 heads over two independent waves halves every per-wave
-// register array (dQ' accumulators, Q, the score tile), so a wave fits in 256
-// registers and two waves share each SIMD: one wave's VALU work (mask, G', dW)
-// overlaps the other's MFMA work.  The waves of one row repeat the cheap
-// per-row work (softmax statistics, record ranking) and need no
-// synchronisation with each other.
+// The 64 heads are split over the two waves of a workgroup (one row per
+// workgroup).  Each wave then needs half the registers (dQ' accumulators, Q,
+// the score tile), so it fits in 256 registers and two waves share each SIMD:
+// one wave's VALU work (mask, G', dW) overlaps the other's MFMA work.  The
+// per-row work that does not depend on the heads is split between the two
+// waves instead of repeated: wave 1 computes the softmax statistics and dI,
+// wave 0 counts and ranks the slots by key range and stores the records; each
+// wave stores half the rows of the shared K tile.  One barrier per chunk.
+// With H <= 32 a single wave does all of it.
 //
 // Per chunk of 32 slots:
 //   GEMM1  S^T[j,h]  = K_g[j,:] . Q[h,:]     v_mfma 32x32x16, M=j N=h K=d; K_g
@@ -40,13 +43,28 @@ namespace {
 
 template <int D>
 struct ExportLds {
-  static constexpr int kPitch = D * 2 + 16;  // bytes per K / Q' row (bank spread)
+  // bytes per K / Q' row: 8 banks of skew per row, so the four rows x 32
+  // bytes of a transposed read fall on distinct LDS banks (a plain XOR
+  // swizzle that also keeps 16-byte stores conflict-free measured no faster)
+  static constexpr int kPitch = D * 2 + 32;
   static constexpr int kTile = kSlots * kPitch;  // one K chunk
-  static constexpr int kStageOff = 2 * kTile;      // two K chunks; Q' staging aliases them
-  static constexpr int kStageBytes = kSlots * 8;  // dI (fp32) + key (int32)
-  static constexpr int kCursorOff = kStageOff + 4 * kStageBytes;
+  // two K tiles (chunks c, c+1); at row start each wave stages its Q' in one
+  static constexpr int kStageOff = 2 * kTile;
+  static constexpr int kStageBytes = kSlots * 8;  // dI (fp32) + key (int32), ring of 4
+  static constexpr int kW1Off = kStageOff + 4 * kStageBytes;  // sign words of wave 1, ring of 2
+  static constexpr int kStatOff = kW1Off + 2 * kSlots * 4;    // m2, invZ
+  static constexpr int kCursorOff = kStatOff + 16;
+  // The range scan keeps one end offset per range in a scratch array that
+  // lives in the K tiles while they are unused, or past the cursor when it
+  // does not fit there (small D with many ranges).
+  __host__ __device__ static int ends_off(int64_t NR) {
+    return NR * 4 <= kStageOff ? 0 : kCursorOff + int(NR) * 4;
+  }
   // dynamic size: the cursor holds one int per key range of the problem
-  static size_t bytes(int64_t NR) { return size_t(kCursorOff) + size_t(NR) * 4; }
+  static size_t bytes(int64_t NR) {
+    const size_t cur = size_t(kCursorOff) + size_t(NR) * 4;
+    return ends_off(NR) == 0 ? cur : cur + size_t(NR) * 4;
+  }
 };
 
 struct Raw {
@@ -68,22 +86,26 @@ __device__ __forceinline__ uint64_t same_range_lanes(bool valid, int r, int nbit
   return same;
 }
 
-template <int D, bool DENSE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void row_export_kernel(
+template <int D, bool DENSE, int NG>
+__global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) void row_export_kernel(
     Problem P) {
   constexpr int KD = D / 16;  // GEMM1 k-steps over d
   constexpr int ND = D / 32;  // GEMM2 32-wide d tiles
   using L = ExportLds<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int half = lane >> 5;
+  // head group of this wave (wave-uniform: readfirstlane keeps it in a scalar)
+  const int g = NG == 2 ? __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)) : 0;
+  // roles: the dI wave (softmax statistics, dI) and the record wave (range
+  // counts, ranking, records); one wave holds both when NG == 1
+  const bool dI_wave = NG == 1 || g == 1;
+  const bool rec_wave = g == 0;
   const int H = int(P.H);
-  const int NG = int(P.HP / 32);
   const int HP = int(P.HP);
-  const int g = int(blockIdx.x % unsigned(NG));
-  const int64_t ridx = int64_t(blockIdx.x / unsigned(NG));
+  const int64_t ridx = int64_t(blockIdx.x);
   // dense rows are visited longest first
   const int64_t r = DENSE ? (P.B * P.S_q - 1 - ridx) : ridx;
   const int64_t b = r / P.S_q;
@@ -102,6 +124,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
   constexpr int RK = kRangeKeys;  // power of two: divisions are shifts
   const int NR = int(P.NR);
   int* cursor = reinterpret_cast<int*>(lds + L::kCursorOff);
+  float* stat = reinterpret_cast<float*>(lds + L::kStatOff);
 
   auto key_of = [&](int j, int id) -> int {
     if (j >= n) return -1;
@@ -109,40 +132,66 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
     return (id >= 0 && id < S_k) ? id : -1;
   };
 
-  // ---- softmax statistics over the valid slots, and the slot count of every
-  //      key range --------------------------------------------------------------
+  int nbits = 0;
+  while ((1 << nbits) < NR) ++nbits;
   const float c2 = P.sm_scale * 1.4426950408889634f;  // base-2 logit scale
-  if (!DENSE) {
+  const float coef = P.grad_loss * P.sm_scale;
+
+  // ---- record wave: slot count of every key range (ballots, no LDS atomics:
+  //      gfx950 runs those at about 190 cycles per instruction for the CU);
+  //      dI wave: softmax statistics.  One pass over the row each. -------------
+  if (rec_wave && !DENSE) {
     for (int i = lane; i < NR; i += 64) cursor[i] = 0;
     wave_lds_sync();
   }
-  int nbits = 0;
-  while ((1 << nbits) < NR) ++nbits;
-  // range counts without LDS atomics (gfx950 runs those at about 190 cycles
-  // per instruction for the whole CU): the lowest lane of every group of
-  // lanes with the same range adds the group's size; leaders have distinct
-  // ranges, so their plain read-modify-writes never collide
-  const float2 st = row_softmax_stats(
-      n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [&](int key) {
-        if (!DENSE) {
+  if (dI_wave) {
+    const float2 st = row_softmax_stats(
+        n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [&](int key) {
+          if (NG == 1 && !DENSE) {
+            const bool valid = key >= 0;
+            const int rg = valid ? key / RK : 0;
+            const uint64_t same = same_range_lanes(valid, rg, nbits);
+            if (valid && (same & lanemask_lt()) == 0) cursor[rg] += __popcll(same);
+            wave_lds_sync();
+          }
+        });
+    if (lane == 0) {
+      stat[0] = st.x;
+      stat[1] = st.y;
+    }
+  } else if (!DENSE) {
+    // record wave of a pair: the counts only
+    constexpr int kU = 8;
+    for (int j0 = 0; j0 < n; j0 += 64 * kU) {
+      int idv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int j = j0 + 64 * u + lane;
+        idv[u] = idrow[j < n ? j : n - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (j0 + 64 * u < n) {
+          const int key = key_of(j0 + 64 * u + lane, idv[u]);
           const bool valid = key >= 0;
           const int rg = valid ? key / RK : 0;
           const uint64_t same = same_range_lanes(valid, rg, nbits);
           if (valid && (same & lanemask_lt()) == 0) cursor[rg] += __popcll(same);
           wave_lds_sync();
         }
-      });
-  const float m2 = st.x, invZ = st.y;
-  const float coef = P.grad_loss * P.sm_scale;
+      }
+    }
+  }
 
-  // ---- range table: range i holds [first_i, end_i), then kSinks sink entries
-  //      with key (i+1)*RK; ranges start at multiples of 4 -------------------
+  // ---- record wave: range table: range i holds [first_i, end_i), then kSinks
+  //      sink entries with key (i+1)*RK; ranges start at multiples of 4 -------
   int2* offrow = reinterpret_cast<int2*>(P.offs) + r * P.NR;
   int2* rkd = reinterpret_cast<int2*>(P.rkd) + r * P.rec_stride;
-  if (DENSE) {
-    // record of slot j at j + kSinks*(j / RK): ranges are already in key order
-    const int nr_used = (n + RK - 1) / RK;
-    if (g == 0) {
+  uint2* rmask = reinterpret_cast<uint2*>(P.rmask) + r * P.rec_stride;
+  if (rec_wave) {
+    if (DENSE) {
+      // record of slot j at j + kSinks*(j / RK): ranges are already in key order
+      const int nr_used = (n + RK - 1) / RK;
       for (int i = lane; i < NR; i += 64) {
         const int cnt = n - i * RK < 0 ? 0 : (n - i * RK < RK ? n - i * RK : RK);
         const int first = i * (RK + kSinks);
@@ -155,38 +204,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
           rkd[i * (RK + kSinks) + cnt + l32] = make_int2((i + 1) * RK, 0);
         }
       }
-    }
-  } else {
-    wave_lds_sync();
-    int* ends = reinterpret_cast<int*>(lds);  // scratch until Q' is staged
-    const int per = (NR + 63) / 64;
-    const int s0 = lane * per < NR ? lane * per : NR;
-    const int s1 = s0 + per < NR ? s0 + per : NR;
-    int sum = 0;
-    for (int i = s0; i < s1; ++i) sum += (cursor[i] + kSinks + 3) & ~3;
-    int incl = sum;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    int run = incl - sum;
-    wave_lds_sync();
-    for (int i = s0; i < s1; ++i) {
-      const int cnt = cursor[i];
-      cursor[i] = run;
-      ends[i] = run + cnt;
-      if (g == 0) offrow[i] = make_int2(run, run + cnt);
-      run += (cnt + kSinks + 3) & ~3;
-    }
-    wave_lds_sync();
-    if (g == 0) {
+    } else {
+      wave_lds_sync();
+      int* ends = reinterpret_cast<int*>(lds + L::ends_off(NR));  // free until Q' is staged
+      const int per = (NR + 63) / 64;
+      const int s0 = lane * per < NR ? lane * per : NR;
+      const int s1 = s0 + per < NR ? s0 + per : NR;
+      int sum = 0;
+      for (int i = s0; i < s1; ++i) sum += (cursor[i] + kSinks + 3) & ~3;
+      int incl = sum;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      int run = incl - sum;
+      wave_lds_sync();
+      for (int i = s0; i < s1; ++i) {
+        const int cnt = cursor[i];
+        cursor[i] = run;
+        ends[i] = run + cnt;
+        offrow[i] = make_int2(run, run + cnt);
+        run += (cnt + kSinks + 3) & ~3;
+      }
+      wave_lds_sync();
       for (int i0 = 0; i0 < NR; i0 += 2) {
         const int i = i0 + half;
         if (i < NR) rkd[ends[i] + l32] = make_int2((i + 1) * RK, 0);
       }
     }
-    wave_lds_sync();
   }
+  __syncthreads();  // statistics published; the ends scratch is free again
+  const float m2 = stat[0], invZ = stat[1];
 
   // ---- per-row operands: this wave's heads -----------------------------------
   const int hl = 32 * g + rotl5(l32);  // head of lane l32 in GEMM1's N dimension
@@ -198,10 +246,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
   for (int kd = 0; kd < KD; ++kd)
     qb1[kd] = hl < H ? *reinterpret_cast<const u32x4_t*>(qrow + hl * D + 8 * half + 16 * kd)
                      : u32x4_t{0u, 0u, 0u, 0u};
-  // (w*q)^T: Q' rows staged in LDS at the natural head offset rotl5(l32), read
-  // back transposed (lane d = 32*nd + l32, 8 heads from 16*ks + 8*half)
+  // (w*q)^T: Q' rows staged in LDS (K tile g of this wave) at the natural head
+  // offset rotl5(l32), read back transposed (lane d = 32*nd + l32, 8 heads
+  // from 16*ks + 8*half)
   {
-    unsigned char* qs = lds;
+    unsigned char* qs = lds + g * L::kTile;
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd) {
       const u32x4_t v = qb1[kd];
@@ -222,35 +271,42 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
             lds_tr8(qs, L::kPitch, r0, r0 + 4, col0);
       }
     }
-    wave_lds_sync();
+    __syncthreads();  // both Q' tiles read before the K tiles take their place
   }
 
   // ---- chunk pipeline ---------------------------------------------------------
   // Iteration c issues GEMM1 of chunk c+1 (K rows already in registers) before
-  // the VALU work of chunk c, so the matrix core and the VALU overlap inside
-  // the wave as well as across the two waves of the SIMD.  Slot data live in
-  // a ring of 4 stages, K rows of chunks c and c+1 in two LDS tiles.
+  // the VALU work of chunk c.  Slot data (dI, key) live in a ring of 4 stages
+  // written by the dI wave, the K rows of chunks c and c+1 in two LDS tiles
+  // of which each wave writes half the rows.  The barrier at the top of an
+  // iteration publishes both, and the record wave's view of wave 1's sign
+  // words of the previous chunk.
   const int nchunks = (n + kSlots - 1) / kSlots;
   auto ktile = [&](int c) -> unsigned char* { return lds + (c & 1) * L::kTile; };
   auto stage_ptr = [&](int c) -> unsigned char* {
     return lds + L::kStageOff + (c & 3) * L::kStageBytes;
   };
+  uint32_t* w1x = reinterpret_cast<uint32_t*>(lds + L::kW1Off);
   auto load_raw = [&](int c) -> Raw {
     const int j = c * kSlots + l32;
     const int jc = j < row_len ? j : row_len - 1;
     Raw v;
     v.id = DENSE ? 0 : idrow[jc];
-    v.I = Irow[jc];
-    v.p = prow[jc];
+    // the record wave of a pair needs only the ids
+    v.I = dI_wave ? Irow[jc] : 0.f;
+    v.p = dI_wave ? prow[jc] : 0.f;
     return v;
   };
-  // dI and key of the lane's slot; lanes l and l+32 publish the same values
+  // key of the lane's slot; the dI wave also publishes dI and key (lanes l and
+  // l+32 write the same values)
   auto finalize = [&](int c, const Raw& v) -> int {
     const int j = c * kSlots + l32;
     const int key = key_of(j, v.id);
-    const float dI = key >= 0 ? slot_dI(v.I, v.p, c2, m2, invZ, coef) : 0.f;
-    reinterpret_cast<float*>(stage_ptr(c))[l32] = dI;
-    reinterpret_cast<int*>(stage_ptr(c) + kSlots * 4)[l32] = key;
+    if (dI_wave) {
+      const float dI = key >= 0 ? slot_dI(v.I, v.p, c2, m2, invZ, coef) : 0.f;
+      reinterpret_cast<float*>(stage_ptr(c))[l32] = dI;
+      reinterpret_cast<int*>(stage_ptr(c) + kSlots * 4)[l32] = key;
+    }
     return key;
   };
   // K rows in GEMM1's A layout: lane holds row l32, d = 8*half + 16*kd + e.
@@ -260,10 +316,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd) kr[kd] = *reinterpret_cast<const u32x4_t*>(src + 16 * kd);
   };
+  // this wave's rows of the K tile (all of them when it is alone)
   auto store_ktile = [&](int c, const u32x4_t (&kr)[KD]) {
+    if (NG == 1 || (l32 >> 4) == g) {
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd)
-      *reinterpret_cast<u32x4_t*>(ktile(c) + l32 * L::kPitch + (8 * half + 16 * kd) * 2) = kr[kd];
+      for (int kd = 0; kd < KD; ++kd)
+        *reinterpret_cast<u32x4_t*>(ktile(c) + l32 * L::kPitch + (8 * half + 16 * kd) * 2) = kr[kd];
+    }
   };
   auto gemm1 = [&](const u32x4_t (&kr)[KD]) -> f32x16_t {
     f32x16_t s = f32x16_t{};
@@ -277,20 +336,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
   for (int nd = 0; nd < ND; ++nd) dqacc[nd] = f32x16_t{};
   float dw_acc = 0.f;
 
-  uint32_t* rmask = P.rmask + 2 * (r * P.rec_stride);
-
-  // Records of chunk c are stored in iteration c+1 after the iteration's one
-  // wait and before its loads: gfx9's vmcnt counts stores too, and a store
-  // issued after a load that is waited for later turns that wait into a full
-  // drain.  Only lanes of valid slots store.
+  // Records of chunk c are stored by the record wave in iteration c+1, after
+  // the iteration's one wait and before its loads (gfx9's vmcnt counts stores
+  // too, and a store issued after a load that is waited for later turns that
+  // wait into a full drain).  Only lanes of valid slots store.
   int prev_pos = 0;
   bool prev_valid = false;
   int2 prev_kd = make_int2(-1, 0);
   uint32_t prev_mask = 0u;
-  auto store_records = [&]() {
-    if (prev_valid) {
-      if (g == 0) rkd[prev_pos] = prev_kd;
-      rmask[2 * prev_pos + g] = prev_mask;
+  auto store_records = [&](int c_prev) {
+    if (rec_wave && prev_valid) {
+      const uint32_t w1 = NG == 2 ? w1x[(c_prev & 1) * kSlots + l32] : 0u;
+      rkd[prev_pos] = prev_kd;
+      rmask[prev_pos] = make_uint2(prev_mask, w1);
     }
   };
 
@@ -308,13 +366,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
 
   // one pipeline step: chunk c with scores s_cur; GEMM1 of chunk c+1 -> s_next
   auto step = [&](int c, const f32x16_t& s_cur, f32x16_t& s_next) {
+    __syncthreads();  // K tile and stage of chunk c complete; chunk c-1 done by both waves
     s_next = gemm1(kr);  // chunk c+1 (padding-only past the end)
     store_ktile(c + 1, kr);
     const int key_n2 = finalize(c + 2, raw);
-    store_records();
+    store_records(c - 1);
     gather(key_n2, kr);
     raw = load_raw(c + 3);
-    wave_lds_sync();
 
     // ---- G' = dI*[S>0], dW, bf16 packing, sign words --------------------------
     // lane: head hl; register 4*i + rr <-> slot 8*i + 4*half + rr
@@ -349,6 +407,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
       gp[i][0] = pack_bf16(gv[0], gv[1]);
       gp[i][1] = pack_bf16(gv[2], gv[3]);
     }
+    if (NG == 2 && g == 1 && lane < kSlots) w1x[(c & 1) * kSlots + lane] = maskword;
 
     // ---- GEMM2: dQ'[h][d] += G'[h][j] K[j][d] ----------------------------------
     // k-step ks covers slots 16*ks + {0..15}; register e of lane (half) is slot
@@ -364,9 +423,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
       }
     }
 
-    // ---- position of every valid slot's record: range start + earlier slots
-    //      of the same range (slot order), identical in both waves of the row --
-    {
+    // ---- record wave: position of every valid slot's record: range start +
+    //      earlier slots of the same range (slot order) -------------------------
+    if (rec_wave) {
       const int key = sk[l32];
       const bool valid = lane < kSlots && key >= 0;
       int pos;
@@ -386,14 +445,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
       prev_kd = make_int2(key, __float_as_int(sd[l32]));
       prev_mask = maskword;
     }
-    wave_lds_sync();
   };
   // unrolled by two: the score tiles alternate without register copies
   for (int c = 0; c < nchunks; c += 2) {
     step(c, sa, sb);
     if (c + 1 < nchunks) step(c + 1, sb, sa);
   }
-  store_records();
+  __syncthreads();  // the last chunk's sign words of wave 1
+  store_records(nchunks - 1);
 
   // ---- row epilogue: dQ = w * dQ', dW -----------------------------------------
   // dQ' register 4*i + rr of lane (half) is GEMM2's row m = 8*i + 4*half + rr,
@@ -418,8 +477,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ro
 
 template <int D, bool DENSE>
 hipError_t launch_t(const Problem& P, hipStream_t stream) {
-  const dim3 grid(unsigned(P.B * P.S_q * (P.HP / 32)));
-  row_export_kernel<D, DENSE><<<grid, 64, ExportLds<D>::bytes(P.NR), stream>>>(P);
+  const dim3 grid(unsigned(P.B * P.S_q));
+  if (P.HP > 32)
+    row_export_kernel<D, DENSE, 2><<<grid, 128, ExportLds<D>::bytes(P.NR), stream>>>(P);
+  else
+    row_export_kernel<D, DENSE, 1><<<grid, 64, ExportLds<D>::bytes(P.NR), stream>>>(P);
   return hipGetLastError();
 }
 

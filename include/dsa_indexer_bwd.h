@@ -120,11 +120,12 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
 /*
  * indexer_bwd_workspace_bytes — device scratch needed by a call with these
  * arguments (dense != 0 selects indexer_bwd_dense; topk is ignored then).
- * The default route needs 16 bytes per record entry (topk + 36 per 256-key
+ * The default route needs 16 bytes per record entry (topk + 36 per 128-key
  * range + 32 entries per row), 8 bytes per row and key range for the range
  * table, (w*q)^T in bf16 (2*H_pad*D bytes per row, H_pad = 32 or 64) and the
- * per query-block dK partial sums (about 370 MB in all at B=1, S_q=8192,
- * S_k=4096, H=64, D=128, topk=1024); IBWD_FLAG_ATOMIC_DK needs none (0).
+ * per query-block dK partial sums (about 460 MB in all at B=1, S_q=8192,
+ * S_k=4096, H=64, D=128, topk=1024; about 860 MB for the dense variant at
+ * that shape); IBWD_FLAG_ATOMIC_DK needs none (0).
  * Returns 0 for invalid shapes as well; the call itself reports those.
  */
 size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_k, int64_t H,
