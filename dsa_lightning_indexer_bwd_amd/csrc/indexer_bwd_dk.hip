@@ -7,30 +7,40 @@
 //
 // Scattering C with fp32 global atomics costs one atomic per (slot, d): 1.05e9
 // at the 8192 x 1024 workload, and gfx950 sustains about 3.3e11 fp32 atomic
-// adds per second whatever the access pattern (LDS float atomics are no
-// faster), so the scatter alone would take milliseconds.  Instead the row
-// kernel exports one record per valid slot {key, dI, the 64 sign bits
-// [S > 0] over h}, grouped by key range, plus (w*q)^T per row; this kernel
-// rebuilds C with bf16 MFMA and reduces it with plain LDS read-modify-write:
+// adds per second whatever the access pattern, so the scatter alone would take
+// milliseconds.  Instead the row kernel exports one record per valid slot
+// {key, dI, the 64 sign bits [S > 0] over h}, grouped by key range, plus
+// (w*q)^T per row, and this kernel computes dK of one key range as a GEMM
+// whose accumulators never leave the matrix cores:
 //
-//   workgroup (key range of 256 keys, query block, batch): an fp32 slab
-//   [256 + 1][D] in LDS (the extra row absorbs the writes of empty tile rows).
-//   Wave w owns the columns 32w .. 32w+31, so no two waves touch the same LDS
-//   word; all waves walk the same stream of 32-slot tiles:
-//     C tile [32 slots x 32 d] = M[32 slots x HP] . (w*q)^T[HP x 32 d]
-//   on v_mfma 32x32x16, with M[slot][h] = [S > 0] in bf16 (0 or 1.0) expanded
-//   from the sign words by two VALU operations per pair of heads, and dI
-//   scaling each slot in fp32.  In the accumulator layout a half-wave holds 32
-//   consecutive columns of one slot, so every LDS read-modify-write touches
-//   32 consecutive words of one slab row per half-wave: with a row pitch of D
-//   words no two lanes of a half-wave share a bank, whatever the keys.
-//   A tile's 32 keys are distinct unless a row repeats an id; a tile with a
-//   repeated key takes an ordered one-row-at-a-time path, so duplicates stay
-//   exact.  The next tile's records and the next query's (w*q)^T are loaded
-//   while the current tile computes.
-// The slab of every (range, query block) goes to global memory, and a last
-// kernel sums the query-block slabs in a fixed order: the result does not
-// depend on scheduling, so d_k is bitwise reproducible.
+//   dK[key][d] = sum over queries t, heads h of A_t[key][h] * Q'_t[h][d],
+//   A_t[key][h] = dI of t's record of key  *  its sign bit of head h
+//                 (0 when t has no record of key),  Q'_t = (w*q)^T of row t.
+//
+//   workgroup (key range of 128 keys, query block, batch), four waves: wave
+//   (kh, ch) owns keys 64kh .. 64kh+63 and columns D/2*ch .. of the range, as
+//   v_mfma 32x32x16 accumulators (64 fp32 registers per lane at D = 128).
+//   Per query with records in the range: wave 0 scatters the records into a
+//   key table in LDS ({dI, sign words, tag}; entries of other queries are told
+//   apart by the tag, so the table is never cleared), the four waves DMA
+//   Q'_t into LDS (global_load_lds, 16 bytes per lane, rows XOR-swizzled so
+//   the 16-byte B-operand reads are bank-conflict free), one barrier, then
+//   every wave expands its A fragments from the table (bf16 dI where the sign
+//   bit is set, three VALU operations per pair of heads) and issues its
+//   MFMAs.  Tables and Q' tiles are double-buffered: the next query's scatter
+//   and DMA run while the current one computes.
+//   A key that a row selects twice (duplicate ids) keeps one record in the
+//   table; wave 0 notices the other by reading the tags back, and after the
+//   query loop the workgroup adds every such record in a pass of its own, in
+//   a fixed order, so the result stays deterministic.
+//   The MFMA work is 2*H*D per (query, key of the range) whether the query
+//   selected the key or not: at 1024 of 4096 keys per query that is four
+//   times the flops of the selected slots, traded for an instruction stream
+//   that is almost all MFMA (a per-slot scatter spends ~60 instructions per
+//   MFMA on LDS read-modify-writes and address arithmetic).
+// The accumulators of every (range, query block) go to global memory, and a
+// last kernel sums the query-block partials in a fixed order: the result does
+// not depend on scheduling, so d_k is bitwise reproducible.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -41,20 +51,37 @@
 namespace ibwd {
 namespace {
 
-constexpr int kTile = 32;  // slots per MFMA tile (M of 32x32x16)
-constexpr int kXcds = 8;   // accelerator dies of the chip, each with its own L2
+constexpr int kXcds = 8;  // accelerator dies of the chip, each with its own L2
 
-template <int D>
+template <int D, int HP>
 struct DkShape {
-  static constexpr int NW = D >= 32 ? D / 32 : 1;  // waves; wave w owns columns 32w..32w+31
-  static constexpr int RK = kRangeKeys;
-  static constexpr int kSlabBytes = (RK + 1) * D * 4;  // row RK: sink of empty tile rows
-  static constexpr int kStampOff = kSlabBytes;
-  static constexpr int kStampStride = RK + 4;  // per wave; entry RK takes inactive lanes
-  static constexpr int kStageOff = kStampOff + NW * kStampStride * 4;  // per wave: 32 int2
-  static constexpr int kListOff = kStageOff + NW * kTile * 8;
-  static constexpr int kBytes = kListOff + kMaxQueryBlock * 16;
-  static_assert(kSlabBytes >= kMaxQueryBlock * 4, "slab doubles as scan scratch");
+  static constexpr int RK = kRangeKeys;        // keys per range (4 blocks of 32)
+  static constexpr int NCB = D / 32;           // 32-column blocks
+  static constexpr int NWC = NCB >= 2 ? 2 : 1; // column groups of waves
+  static constexpr int NWK = 2;                // key groups of waves
+  static constexpr int NW = NWK * NWC;         // MMA waves (plus one producer wave)
+  static constexpr int NTH = 64 * (NW + 1);
+  static constexpr int KBW = RK / 32 / NWK;    // key blocks per wave
+  static constexpr int CBW = NCB / NWC;        // column blocks per wave
+  static constexpr int KS = HP / 16;           // 16-deep k-steps over the heads
+  static constexpr int kRowBytes = HP * 2;     // one d row of (w*q)^T
+  static constexpr int kCpr = kRowBytes / 16;  // 16-byte chunks per row
+  static constexpr int kQBytes = D * kRowBytes;
+  static constexpr int kTOff = 3 * kQBytes;    // three Q' tiles, then two key tables
+  static constexpr int kStOff = kTOff + 2 * RK * 16;  // four record stages {kd, w}
+  static constexpr int kStBytes = 2 * kRecBlock * 8;
+  static constexpr int kListOff = kStOff + 4 * kStBytes;
+  static constexpr int kFlagOff = kListOff + kMaxQueryBlock * 16;
+  static constexpr int kBytes = kFlagOff + 16;
+  static constexpr int kDmaQ = kQBytes / 1024;  // copies of 64 lanes x 16 B per Q' tile
+  static constexpr int kDmaW = kDmaQ / NW;       // ... issued by each MMA wave
+  static constexpr int kFbTag = 16382;         // pass id of the duplicate passes
+  // (query passes use 0 .. kMaxQueryBlock-1; 16383 marks a never-written entry)
+  static_assert(kDmaW * NW * 1024 == kQBytes, "Q' tile splits into whole copies per wave");
+  static_assert(kDmaW < 64, "one iteration's copies fit a vmcnt immediate");
+  static_assert(3 * kQBytes >= kMaxQueryBlock * 4, "Q' tiles double as scan scratch");
+  static_assert(kRecBlock * 8 == 1024, "one DMA moves a record block of one array");
+  static_assert(KBW * 32 * NWK == RK, "key blocks cover the range");
 };
 
 // Exclusive prefix sum over a[0..n) in LDS by one wave, in place; returns the total.
@@ -81,38 +108,61 @@ __device__ int wave_exclusive_scan(int* a, int n) {
   return __shfl(incl, 63, 64);
 }
 
-// Records of one 32-slot tile.  MFMA row m (the A operand's lane m = l32)
-// takes record base + pi(m), pi(8i + 4h + r) = 16h + 4i + r, so that
-// accumulator register 4i + r of a lane in half h is the record
-// base + 16h + 4i + r.  A lane loads only the record of its MFMA row (lanes l
-// and l+32 the same one); the keys and dI of its 16 accumulator rows come
-// from a per-wave LDS stage, where the 32 records of the tile are four
-// 16-byte broadcast reads per half-wave away.  (Loading them from global
-// memory per lane would move 16 times the tile's bytes through the vector
-// memory path.)
-// Entries past a range's end are sinks (key one past the range), so a tile
-// needs no bounds checks: sink rows land in the slab's scratch row RK.
-struct Tile {
-  uint2 w;   // sign words of record base + pi(l32)
-  int2 kd;   // {key, dI bits} of record base + pi(l32)
-};
+// s_waitcnt vmcnt(n) (n < 16), leaving the other counters alone.  Vector
+// memory operations of a wave complete in issue order, so this waits for all
+// but the last n the wave issued.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt immediate");  // bits 3:0 and 15:14
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
+// 64 lanes x 16 bytes from global memory (gbase + voff per lane) straight into
+// LDS bytes lds_addr + 16*lane (global_load_lds_dwordx4; the LDS base goes in
+// M0).  Written as assembly so that the compiler neither inserts waits for it
+// (it would wait for the copy before every later LDS read, the copy's own
+// destination or not) nor counts it: the kernel waits for these copies itself,
+// and the compiler's own vmcnt waits stay correct, only more conservative.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, const void* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
+// Byte offset of chunk (16 bytes) c of row d of a Q' tile in LDS: the chunk
+// index is XORed with bits of the row so that eight consecutive rows read at
+// one chunk (one 16-byte B-operand read of eight lanes) hit distinct banks.
+template <int HP>
+__device__ __forceinline__ int qt_swz(int d, int c) {
+  constexpr int kCpr = HP / 8;
+  const int f = ((d * HP * 2) >> 7) & (kCpr - 1);
+  return d * HP * 2 + ((c ^ f) << 4);
+}
 
 template <int NH, int D>
-__global__ __launch_bounds__(64 * DkShape<D>::NW, 2) void dk_range_kernel(Problem P) {
-  using S = DkShape<D>;
-  constexpr int KS = NH * 2;  // 16-deep k-steps over the heads
+// Two workgroups of NW + 1 waves share a CU: three waves per SIMD, so at most
+// 168 registers per lane.
+__global__ __launch_bounds__((DkShape<D, NH * 32>::NTH)) __attribute__((amdgpu_waves_per_eu(3))) void
+dk_range_kernel(Problem P) {
   constexpr int HP = NH * 32;
-  constexpr int NTH = 64 * S::NW;
+  using S = DkShape<D, HP>;
+  constexpr int KS = S::KS;
+  constexpr int NTH = S::NTH;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  float* slab = reinterpret_cast<float*>(lds);
   int4* list = reinterpret_cast<int4*>(lds + S::kListOff);
-  __shared__ int nne_s;
+  int* flags = reinterpret_cast<int*>(lds + S::kFlagOff);  // count, duplicates, losers
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int half = lane >> 5;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // waves 0 .. NW-1 own keys 64kh.. x columns .. and copy Q' tiles into LDS;
+  // wave NW produces the key tables (copies the records, scatters them,
+  // checks for duplicate keys) and does no MMA
+  const bool prod = wv == S::NW;
+  const int kh = wv % S::NWK, ch = (wv / S::NWK) % S::NWC;
   // Workgroup i is dispatched to XCD i % 8.  Consecutive logical ids (the key
   // ranges of one query block) are given to workgroups of one XCD, so the
   // (w*q)^T rows that every range of the block reads are fetched into that
@@ -131,13 +181,16 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 2) void dk_range_kernel(Proble
   }
   const int RK = S::RK;
   const int R0 = R * RK;
-  const int nkeys = int(P.S_k - R0 < RK ? P.S_k - R0 : RK);
   const int64_t t0 = int64_t(qb) * P.QBS;
   const int nq = int((t0 + P.QBS < P.S_q ? t0 + P.QBS : P.S_q) - t0);
 
+  // key tables: no entry carries a pass id of this launch yet
+  for (int i = tid; i < 2 * RK; i += NTH)
+    reinterpret_cast<uint4*>(lds + S::kTOff)[i] = make_uint4(0, 0, 0, 0xffffffffu);
+
   // ---- the block's queries that have records in this range ------------------
   {
-    int* flag = reinterpret_cast<int*>(lds);  // scratch in the slab area
+    int* flag = reinterpret_cast<int*>(lds);  // scratch in the Q' tiles
     int4 mine[(kMaxQueryBlock + NTH - 1) / NTH];
 #pragma unroll
     for (int u = 0; u < (kMaxQueryBlock + NTH - 1) / NTH; ++u) {
@@ -152,7 +205,10 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 2) void dk_range_kernel(Proble
     __syncthreads();
     if (wv == 0) {
       const int nne = wave_exclusive_scan(flag, nq);  // flag := compacted index
-      if (lane == 0) nne_s = nne;
+      if (lane == 0) {
+        flags[0] = nne;
+        flags[1] = 0;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -162,171 +218,288 @@ __global__ __launch_bounds__(64 * DkShape<D>::NW, 2) void dk_range_kernel(Proble
     }
     __syncthreads();
   }
-  const int nne = nne_s;
+  const int nne = __builtin_amdgcn_readfirstlane(flags[0]);
 
-  for (int i = tid; i < (RK + 1) * D; i += NTH) slab[i] = 0.f;
-  int* stamp = reinterpret_cast<int*>(lds + S::kStampOff) + wv * S::kStampStride;
-  for (int i = lane; i < S::kStampStride; i += 64) stamp[i] = 0;
-  __syncthreads();
-
-  const int col = 32 * wv + l32;  // the lane's slab column
-  // A-operand expansion: element pair j of k-step ks sits at bits q and q + 16
-  // of the sign word shifted right by 8*(ks & 1), q = 4*half + j
-  uint32_t emask[4], emul[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    emask[j] = 0x10001u << (4 * half + j);
-    emul[j] = 0x3f80u >> (4 * half + j);
-  }
-  const int pim = 16 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
-
-  // B operand: (w*q)^T, lane holds d = col, h = 16*ks + 8*half + e
-  // Query-level values (list entries) are wave-uniform: moving them to scalar
-  // registers makes every record and (w*q)^T address a scalar row base plus a
-  // 32-bit per-lane offset.
+  // ---- operand helpers --------------------------------------------------------
   auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-  const uint32_t qt_lane = uint32_t((col * HP + 8 * half) * 2);
-  auto load_qt = [&](int row, u32x4_t (&a)[KS]) {
-    const char* qtrow = reinterpret_cast<const char*>(P.qt) + size_t(uni(row)) * (D * HP * 2);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      a[ks] = *reinterpret_cast<const u32x4_t*>(qtrow + qt_lane + 32 * ks);
+  const uint32_t lds0 = uint32_t(uintptr_t((__attribute__((address_space(3))) unsigned char*)(lds)));
+  auto qtile = [&](int buf) { return lds + buf * S::kQBytes; };
+  auto table = [&](int buf) { return reinterpret_cast<uint4*>(lds + S::kTOff + buf * RK * 16); };
+  auto stage_kd = [&](int buf) { return reinterpret_cast<const int2*>(lds + S::kStOff + buf * S::kStBytes); };
+  auto stage_w = [&](int buf) {
+    return reinterpret_cast<const uint2*>(lds + S::kStOff + buf * S::kStBytes + kRecBlock * 8);
   };
-  // records of the tile starting at `base` (at most 31 entries past the
-  // range's end: inside its sink entries)
-  auto load_tile = [&](int row, int base) -> Tile {
-    Tile tl;
-    const size_t rb = size_t(uni(row)) * size_t(P.rec_stride) * 8;
-    const uint32_t ia = uint32_t(uni(base) + pim) * 8;
-    tl.w = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(P.rmask) + rb + ia);
-    tl.kd = *reinterpret_cast<const int2*>(reinterpret_cast<const char*>(P.rkd) + rb + ia);
-    return tl;
+  // MMA wave wv: its kDmaW KiB of Q'_t of row `row` into tile `buf`; lane i
+  // of each copy fills LDS bytes 16i.. of its KiB with the global chunk the
+  // XOR swizzle puts there (the swizzle term depends on the lane only)
+  uint32_t dma_lane;
+  {
+    const int pl = 16 * lane;
+    const int c = (pl & (S::kRowBytes - 1)) >> 4;
+    const int f = (pl >> 7) & (S::kCpr - 1);
+    dma_lane = uint32_t((pl & ~(S::kRowBytes - 1)) | ((c ^ f) << 4));
+  }
+  auto dma_qt = [&](int row, int buf) {
+    const unsigned char* src =
+        reinterpret_cast<const unsigned char*>(P.qt) + size_t(uni(row)) * S::kQBytes;
+#pragma unroll
+    for (int j = 0; j < S::kDmaW; ++j) {
+      const int kib = wv * S::kDmaW + j;
+      dma16(lds0 + uint32_t(buf * S::kQBytes + kib * 1024), src + kib * 1024, dma_lane);
+    }
   };
-  int2* stage = reinterpret_cast<int2*>(lds + S::kStageOff) + wv * kTile;
+  // producer: records first .. first+kRecBlock-1 of row `row` into stage `buf`
+  // (two DMAs: {key, dI} and the sign words; records past the range's end are
+  // read and ignored)
+  auto dma_recs = [&](int row, int first, int buf) {
+    const size_t r0 = size_t(uni(row)) * size_t(P.rec_stride) + size_t(uni(first));
+    const uint32_t st = lds0 + uint32_t(S::kStOff + buf * S::kStBytes);
+    dma16(st, reinterpret_cast<const char*>(P.rkd) + r0 * 8, uint32_t(16 * lane));
+    dma16(st + kRecBlock * 8, reinterpret_cast<const char*>(P.rmask) + r0 * 8, uint32_t(16 * lane));
+  };
+  auto rec_kd = [&](int row, int r) {
+    return reinterpret_cast<const int2*>(P.rkd)[size_t(row) * size_t(P.rec_stride) + r];
+  };
+  auto rec_w = [&](int row, int r) {
+    return reinterpret_cast<const uint2*>(P.rmask)[size_t(row) * size_t(P.rec_stride) + r];
+  };
+  auto tag_of = [](int pid, int r) { return uint32_t(pid) << 18 | uint32_t(r); };
 
-  // one tile of records tl with B operand qa
-  auto process = [&](const Tile& tl, const u32x4_t (&qa)[KS]) {
-    // are the tile's keys pairwise distinct?  Each lane of the lower half
-    // writes its lane number at its key's stamp and reads it back (one wave's
-    // LDS accesses run in order): lanes that share a key read the one lane
-    // number that won, so all but one of them see a clash.  Lanes of the upper
-    // half and sinks (key - R0 == RK) use the spare entry RK and do not count.
-    // Stamps are per wave.
-    const int ka = tl.kd.x;
-    const bool active = half == 0 && ka - R0 < RK;
-    int* sp = &stamp[active ? ka - R0 : RK];
-    *sp = lane;
-    if (half == 0) stage[pim] = tl.kd;
-    wave_lds_sync();
-    const int stamp_old = *sp;
-    // keys and dI of the lane's accumulator rows base + 16*half + 4i + (0..3)
-    int4 key[4];
-    float4 di[4];
+  // accumulators: key block kb (keys 32*(KBW*kh + kb) + 8i + 4half + r in
+  // register 4i + r), column block cb (column 32*(CBW*ch + cb) + l32)
+  f32x16_t acc[S::KBW][S::CBW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int4 a = *reinterpret_cast<const int4*>(stage + 16 * half + 4 * i);
-      const int4 c = *reinterpret_cast<const int4*>(stage + 16 * half + 4 * i + 2);
-      key[i] = make_int4(a.x, a.z, c.x, c.z);
-      di[i] = make_float4(__int_as_float(a.y), __int_as_float(a.w), __int_as_float(c.y),
-                          __int_as_float(c.w));
-    }
+  for (int kb = 0; kb < S::KBW; ++kb)
+#pragma unroll
+    for (int cb = 0; cb < S::CBW; ++cb) acc[kb][cb] = f32x16_t{};
 
-    f32x16_t acc = f32x16_t{};
+  // one query's (or one duplicate record's) contribution: A from key table
+  // `tb` (entries tagged with pass `pid`), B = Q' tile `qbuf`
+  auto mfma_pass = [&](int tb, int qbuf, int pid) {
+    const uint4* T = table(tb);
+    const unsigned char* Q = qtile(qbuf);
+    u32x4_t bop[S::CBW][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t word = (ks < 2 ? tl.w.x : tl.w.y) >> (8 * (ks & 1));
-      u32x4_t av;
+    for (int cb = 0; cb < S::CBW; ++cb) {
+      const int d = 32 * (S::CBW * ch + cb) + l32;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) av[j] = __umul24(word & emask[j], emul[j]);
-      acc = mfma32(av, qa[ks], acc);
+      for (int ks = 0; ks < KS; ++ks)
+        bop[cb][ks] = *reinterpret_cast<const u32x4_t*>(Q + qt_swz<HP>(d, 2 * ks + half));
     }
-
-    // accumulator register 4i + r: record base + 16*half + 4i + r, column col;
-    // byte offsets into the slab (the sink key R0 + RK lands on row RK)
-    const int cbase = (col - R0 * D) * 4;
-    int addr[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      addr[4 * i + 0] = key[i].x * (D * 4) + cbase;
-      addr[4 * i + 1] = key[i].y * (D * 4) + cbase;
-      addr[4 * i + 2] = key[i].z * (D * 4) + cbase;
-      addr[4 * i + 3] = key[i].w * (D * 4) + cbase;
-    }
-    auto at = [&](int k) -> float& { return *reinterpret_cast<float*>(lds + addr[k]); };
-    const float dv[16] = {di[0].x, di[0].y, di[0].z, di[0].w, di[1].x, di[1].y, di[1].z, di[1].w,
-                          di[2].x, di[2].y, di[2].z, di[2].w, di[3].x, di[3].y, di[3].z, di[3].w};
-    const bool clash = active && stamp_old != lane;
-    if (ballot(clash) == 0) {
-      float old[16];
+    for (int kb = 0; kb < S::KBW; ++kb) {
+      const uint4 e = T[32 * (S::KBW * kh + kb) + l32];
+      const bool valid = (e.w >> 18) == uint32_t(pid);
+      // bf16 dI where the sign bit is set: ((word >> p) & 0x10001) * dI_bf16
+      // puts dI in both halves of a pair of heads at once
+      const uint32_t dib = valid ? (pack_bf16(__uint_as_float(e.x), 0.f) & 0xffffu) : 0u;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) old[k] = at(k);
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t word = (ks < 2 ? e.y : e.z) >> (8 * (ks & 1) + 4 * half);
+        u32x4_t a;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) at(k) = fmaf(dv[k], acc[k], old[k]);
-    } else {
-      // ordered path: one slab row (one register of one half-wave) at a time
-      for (int k = 0; k < 16; ++k) {
-        for (int hh = 0; hh < 2; ++hh) {
-          if (half == hh) at(k) = fmaf(dv[k], acc[k], at(k));
-          wave_lds_sync();
-        }
+        for (int j = 0; j < 4; ++j) a[j] = __umul24((word >> j) & 0x10001u, dib);
+#pragma unroll
+        for (int cb = 0; cb < S::CBW; ++cb) acc[kb][cb] = mfma32(a, bop[cb][ks], acc[kb][cb]);
       }
     }
   };
-  // all tiles of one query; f is its first tile, loaded a query earlier.
-  // Tiles are prefetched one ahead with the loop unrolled by two so that no
-  // loaded register is copied (a copy would wait for the load).
-  auto run_query = [&](const int4 el, const u32x4_t (&qa)[KS], const Tile& f) {
-    // the entry in scalar registers: no LDS read (and no wait behind the
-    // previous tile's slab writes) inside the tile loop
-    const int4 e = make_int4(uni(el.x), uni(el.y), uni(el.z), 0);
-    const int ntl = (e.z - e.y + kTile - 1) / kTile;
-    const int last = e.y + kTile * (ntl - 1);
-    auto tbase = [&](int tt) { return e.y + kTile * tt < last ? e.y + kTile * tt : last; };
-    Tile tb = load_tile(e.x, tbase(1));
-    process(f, qa);
-    for (int tt = 1; tt < ntl; tt += 2) {
-      const Tile ta = load_tile(e.x, tbase(tt + 1));
-      process(tb, qa);
-      tb = load_tile(e.x, tbase(tt + 2));
-      if (tt + 1 < ntl) process(ta, qa);
+
+  // (Keys of records of range R lie in [R0, R0 + RK); the table index is
+  // masked anyway, so that no record can address LDS outside the table.)
+  // producer: scatter the records of list entry e (staged in `sbuf`) into table
+  // tb, tagged pid, in record order (so a key written twice keeps the later
+  // record, the same way in every scatter of these records).  Records past
+  // the staged block (only with duplicate keys) come from global memory.
+  auto scatter = [&](int4 e, int sbuf, int tb, int pid, int (&key)[2]) {
+    uint4* T = table(tb);
+    const int n = uni(e.z) - uni(e.y);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 64 * h + lane;
+      key[h] = R0;
+      if (r < n) {
+        const int2 kd = stage_kd(sbuf)[r];
+        const uint2 w = stage_w(sbuf)[r];
+        key[h] = kd.x;
+        T[(kd.x - R0) & (RK - 1)] = make_uint4(uint32_t(kd.y), w.x, w.y, tag_of(pid, r));
+      }
+    }
+    for (int c0 = kRecBlock; c0 < n; c0 += 64) {
+      wave_lds_sync();
+      if (c0 + lane < n) {
+        const int2 kd = rec_kd(e.x, e.y + c0 + lane);
+        const uint2 w = rec_w(e.x, e.y + c0 + lane);
+        T[(kd.x - R0) & (RK - 1)] = make_uint4(uint32_t(kd.y), w.x, w.y, tag_of(pid, c0 + lane));
+      }
     }
   };
+  // producer: did a record of a query with n records (keys key[], as the
+  // scatter returned them) lose its entry of table tb (pass pid) to a later
+  // record of the same key?
+  auto lost_any = [&](int n, const int (&key)[2], int tb, int pid) {
+    const uint4* T = table(tb);
+    bool lost = false;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 64 * h + lane;
+      if (r < n) lost = lost || T[(key[h] - R0) & (RK - 1)].w != tag_of(pid, r);
+    }
+    return ballot(lost) != 0 || n > kRecBlock;  // more records than keys: duplicates
+  };
 
-  if (nne > 0) {
-    // queries alternate between two operand sets, each loaded one query ahead
-    u32x4_t qa0[KS], qa1[KS];
-    Tile f0, f1;
-    {
+  // ---- query loop ---------------------------------------------------------------
+  // Query qi: Q' tile qi % 3 (copied two queries ahead by the MMA waves),
+  // record stage qi % 4 (copied three queries ahead by the producer), key
+  // table qi % 2 (built by the producer right after the barrier of query
+  // qi-1, from the staged records).  Every wave issues its copies and no other
+  // vector-memory operation in the loop (except the producer's loads of
+  // records past a staged block, which the compiler waits for at once), so
+  // "all but the previous iteration's copies" is one vmcnt immediate.  The
+  // two roles run separate loops (so that their registers need not be live at
+  // once), each with one barrier per query.
+  bool dup = false;  // producer: some record lost its table entry to a duplicate key
+  if (prod) {
+    auto wait_prev = [&](bool issued) {
+      if (issued)
+        wait_vm<2>();
+      else
+        wait_vm<0>();
+    };
+    int key[2];  // keys of the last scattered query's records
+    if (nne > 0) {
       const int4 e0 = list[0];
-      const int4 e1 = list[nne > 1 ? 1 : 0];
-      load_qt(e0.x, qa0);
-      f0 = load_tile(e0.x, e0.y);
-      load_qt(e1.x, qa1);
-      f1 = load_tile(e1.x, e1.y);
+      dma_recs(e0.x, e0.y, 0);
+      if (nne > 1) dma_recs(uni(list[1].x), uni(list[1].y), 1);
+      // the copy of "iteration -1": records(2)
+      if (nne > 2) dma_recs(uni(list[2].x), uni(list[2].y), 2);
+      wait_prev(nne > 2);  // records(0), records(1) are in
+      scatter(e0, 0, 0, 0, key);
     }
-    for (int qi = 0; qi < nne; qi += 2) {
-      run_query(list[qi], qa0, f0);
-      {
-        const int4 e2 = list[qi + 2 < nne ? qi + 2 : nne - 1];
-        load_qt(e2.x, qa0);
-        f0 = load_tile(e2.x, e2.y);
-      }
-      if (qi + 1 < nne) run_query(list[qi + 1], qa1, f1);
-      {
-        const int4 e3 = list[qi + 3 < nne ? qi + 3 : nne - 1];
-        load_qt(e3.x, qa1);
-        f1 = load_tile(e3.x, e3.y);
-      }
+    // list entries are read one iteration before they are needed
+    int4 e_cur = nne > 0 ? list[0] : make_int4(0, 0, 0, 0);
+    int4 e_n1 = nne > 1 ? list[1] : e_cur;
+    int4 e_n3 = nne > 3 ? list[3] : e_cur;
+    for (int qi = 0; qi < nne; ++qi) {
+      // the copy of iteration qi-1 is records(qi+2) if qi+2 < nne; records(qi+1)
+      // is in
+      wait_prev(qi + 2 < nne);
+      __syncthreads();  // table qi % 2 is complete; query qi-1 is done
+      const int4 e1 = e_n1, e3 = e_n3;
+      const int n = uni(e_cur.z) - uni(e_cur.y);
+      e_cur = e1;
+      if (qi + 2 < nne) e_n1 = list[qi + 2];
+      if (qi + 4 < nne) e_n3 = list[qi + 4];
+      // duplicates of query qi: read its table entries back (its table stays
+      // intact until the scatter of query qi+2, one iteration later)
+      const int kq[2] = {key[0], key[1]};
+      // table of query qi+1: its last readers finished query qi-1
+      if (qi + 1 < nne) scatter(e1, (qi + 1) & 3, (qi + 1) & 1, qi + 1, key);
+      dup = dup || lost_any(n, kq, qi & 1, qi);
+      // stage (qi+3) % 4 = (qi-1) % 4 was last read by the scatter of query
+      // qi-1, whose table writes waited for those reads
+      if (qi + 3 < nne) dma_recs(uni(e3.x), uni(e3.y), (qi + 3) & 3);
+    }
+  } else {
+    auto wait_prev = [&](bool issued) {
+      if (issued)
+        wait_vm<S::kDmaW>();
+      else
+        wait_vm<0>();
+    };
+    if (nne > 0) {
+      dma_qt(list[0].x, 0);
+      // the copy of "iteration -1": Q'(1)
+      if (nne > 1) dma_qt(list[1].x, 1);
+    }
+    int q0 = 0, q2 = 2;  // qi % 3, (qi+2) % 3
+    int row2 = nne > 2 ? list[2].x : 0;  // read one iteration before it is needed
+    for (int qi = 0; qi < nne; ++qi) {
+      // the copy of iteration qi-1 is Q'(qi+1) if qi+1 < nne; this wave's
+      // share of Q'(qi) is in
+      wait_prev(qi + 1 < nne);
+      __syncthreads();  // every share of Q'(qi), and table qi % 2, are complete
+      // Q' tile (qi+2) % 3 was last read in query qi-1
+      const int r2 = row2;
+      if (qi + 3 < nne) row2 = list[qi + 3].x;
+      if (qi + 2 < nne) dma_qt(r2, q2);
+      mfma_pass(qi & 1, q0, qi);
+      q0 = q0 == 2 ? 0 : q0 + 1;
+      q2 = q2 == 2 ? 0 : q2 + 1;
     }
   }
+
+  // ---- records that lost their table entry to a duplicate key --------------------
+  // Rare (a row that selects one key more than once).  Per query: rebuild its
+  // table the same way (same winners), list the losers, and add each in a pass
+  // of its own through the spare table, in record order.
+  if (prod && lane == 0 && dup) flags[1] = 1;
   __syncthreads();
-  // slab -> global partial of this (range, query block)
-  float* dst = P.slab + ((b * P.NQB + qb) * (P.NR * RK) + R0) * D;
-  for (int i = tid; i < nkeys * (D / 4); i += NTH) {
-    const int kr = i / (D / 4), c4 = i % (D / 4);
-    const float4 v = *reinterpret_cast<const float4*>(slab + kr * D + 4 * c4);
-    *reinterpret_cast<float4*>(dst + kr * D + 4 * c4) = v;
+  if (flags[1] != 0) {
+    int* losers = reinterpret_cast<int*>(qtile(1));  // 64 record indices per round
+    for (int i = tid; i < 2 * RK; i += NTH) table(0)[i] = make_uint4(0, 0, 0, 0xffffffffu);
+    for (int qi = 0; qi < nne; ++qi) {
+      __syncthreads();
+      const int4 e = list[qi];
+      if (prod) {
+        dma_recs(e.x, e.y, 0);
+        wait_vm<0>();
+        int kq[2];
+        scatter(e, 0, 0, S::kFbTag, kq);
+      } else {
+        dma_qt(e.x, 0);
+        wait_vm<0>();
+      }
+      __syncthreads();
+      const int n = uni(e.z) - uni(e.y);
+      for (int c0 = 0; c0 < n; c0 += 64) {
+        if (prod) {
+          bool lost = false;
+          if (c0 + lane < n) {
+            const int2 kd = rec_kd(e.x, e.y + c0 + lane);
+            lost = table(0)[(kd.x - R0) & (RK - 1)].w != tag_of(S::kFbTag, c0 + lane);
+          }
+          const uint64_t m = ballot(lost);
+          if (lost) losers[__popcll(m & lanemask_lt())] = c0 + lane;
+          if (lane == 0) flags[2] = __popcll(m);
+        }
+        __syncthreads();
+        const int nl = uni(flags[2]);
+        for (int li = 0; li < nl; ++li) {
+          const int r = uni(losers[li]);
+          if (prod && lane == 0) {
+            const int2 kd = rec_kd(e.x, e.y + r);
+            const uint2 w = rec_w(e.x, e.y + r);
+            table(1)[(kd.x - R0) & (RK - 1)] =
+                make_uint4(uint32_t(kd.y), w.x, w.y, tag_of(S::kFbTag, r));
+          }
+          __syncthreads();
+          if (!prod) mfma_pass(1, 0, S::kFbTag);
+          __syncthreads();
+          if (prod && lane == 0)
+            table(1)[(rec_kd(e.x, e.y + r).x - R0) & (RK - 1)] = make_uint4(0, 0, 0, 0xffffffffu);
+        }
+        __syncthreads();
+      }
+    }
   }
+
+  // ---- accumulators -> this (range, query block)'s partial dK ------------------
+  if (prod) return;
+  float* dst = P.slab + ((b * P.NQB + qb) * (P.NR * RK) + R0) * D;
+#pragma unroll
+  for (int kb = 0; kb < S::KBW; ++kb)
+#pragma unroll
+    for (int cb = 0; cb < S::CBW; ++cb) {
+      const int col = 32 * (S::CBW * ch + cb) + l32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kl = 32 * (S::KBW * kh + kb) + 8 * i + 4 * half + r;
+          if (R0 + kl < P.S_k) dst[size_t(kl) * D + col] = acc[kb][cb][4 * i + r];
+        }
+    }
 }
 
 // d_k[b][s][:] = sum over query blocks (in order) of the slabs.
@@ -353,12 +526,12 @@ __global__ __launch_bounds__(256) void dk_sum_kernel(Problem P) {
 
 template <int NH, int D>
 hipError_t launch_dk_t(const Problem& P, hipStream_t stream) {
-  using S = DkShape<D>;
+  using S = DkShape<D, NH * 32>;
   const dim3 grid(unsigned(P.NR * P.NQB * P.B));
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&dk_range_kernel<NH, D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::kBytes);
   if (err != hipSuccess) return err;
-  dk_range_kernel<NH, D><<<grid, 64 * S::NW, S::kBytes, stream>>>(P);
+  dk_range_kernel<NH, D><<<grid, S::NTH, S::kBytes, stream>>>(P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   stage_done(1, "dk_range_kernel");
   const int64_t n4 = P.B * P.S_k * P.D / 4;

@@ -14,6 +14,7 @@ constexpr int kRangeKeys = 128;     // keys per range of the two-pass dK route
 constexpr int kSinks = 32;          // sink entries after every range's records
 constexpr int kMaxRanges = 2048;    // ranges a row can be bucketed into (S_k <= 262144)
 constexpr int kMaxQueryBlock = 512;  // queries per range-kernel workgroup
+constexpr int kRecBlock = 128;       // records the range kernel stages per DMA
 
 enum DkRoute : int {
   kDkTwoPass = 0,  // masks + records exported, range-major LDS reduction (deterministic)
@@ -60,11 +61,13 @@ inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_
   L.NQB = (S_q + L.QBS - 1) / L.QBS;
   L.nchunk = (row_len + kSlots - 1) / kSlots;
   const size_t recs = size_t(L.rows) * size_t(L.rec_stride);
+  // the range kernel moves records in blocks of kRecBlock, which may run past
+  // the last row's records: each record array is followed by one block of slack
   size_t o = 0;
   L.off_rkd = o;
-  o = align256(o + recs * 8);
+  o = align256(o + recs * 8 + kRecBlock * 8);
   L.off_rmask = o;
-  o = align256(o + recs * 8);
+  o = align256(o + recs * 8 + kRecBlock * 8);
   L.off_offs = o;
   o = align256(o + size_t(L.rows) * size_t(L.NR) * 8);
   L.off_qt = o;

@@ -45,9 +45,11 @@
  *     stream as usual for HIP.
  *   - dK routes.  The default route reduces the dK scatter in two passes: the
  *     row kernel exports each slot's sign mask [S > 0] and dI into the caller's
- *     workspace, and a range-major kernel rebuilds and sums the contributions
- *     in on-chip memory, then the per query-block partial sums are added in a
- *     fixed order.  d_q, d_w and d_k are all bitwise reproducible run to run.
+ *     workspace, and a range-major kernel computes the dK of every 128-key
+ *     range as a GEMM over (query, head) whose accumulators stay in the matrix
+ *     cores (dI enters that GEMM rounded to bf16, like w*q), then the per
+ *     query-block partial sums are added in a fixed order.  d_q, d_w and d_k
+ *     are all bitwise reproducible run to run.
  *     IBWD_FLAG_ATOMIC_DK selects the single-pass route of the pages' design
  *     instead: fp32 global atomics straight from the row kernel, no workspace,
  *     and d_k may then differ in the last bits between runs (PR #549: dK uses
