@@ -43,11 +43,34 @@ namespace {
 
 template <int D>
 struct ExportLds {
-  // bytes per K / Q' row: 8 banks of skew per row, so the four rows x 32
-  // bytes of a transposed read fall on distinct LDS banks (a plain XOR
-  // swizzle that also keeps 16-byte stores conflict-free measured no faster)
-  static constexpr int kPitch = D * 2 + 32;
+  // K / Q' rows are stored unpadded with their 16-byte chunks permuted by an
+  // XOR of the row (D >= 64): eight rows read or written at one chunk (16
+  // bytes per lane) and the four rows x 32 bytes of a transposed read then
+  // fall on distinct LDS banks.  D = 32 rows (four chunks) are padded instead.
+  static constexpr bool kSwz = D >= 64;
+  static constexpr int kPitch = kSwz ? D * 2 : D * 2 + 32;
   static constexpr int kTile = kSlots * kPitch;  // one K chunk
+  // byte offset of byte `byte` of row `row` (16-byte accesses stay whole)
+  __device__ static int at(int row, int byte) {
+    const int f = kSwz ? (((row & 3) << 1) | ((row >> 2) & 1)) : 0;
+    return row * kPitch + (((byte >> 4) ^ f) << 4) + (byte & 15);
+  }
+  // ds_read_b64_tr_b16 of a 4 x 16 block (rows row0.., bf16 columns col0..):
+  // source lane s of each 16-lane group points at row row0 + s/4, columns
+  // col0 + 4*(s%4) .. +3
+  __device__ static uint2 tr4(const unsigned char* tile, int row0, int col0) {
+    const int s = threadIdx.x & 15;
+    const unsigned char* a = tile + at(row0 + (s >> 2), (col0 + 4 * (s & 3)) * 2);
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(a));
+    return __builtin_bit_cast(uint2, v);
+  }
+  // an MFMA operand of 8 k-values: rows [r0, r0+4) then [r1, r1+4)
+  __device__ static u32x4_t tr8(const unsigned char* tile, int r0, int r1, int col0) {
+    const uint2 x = tr4(tile, r0, col0);
+    const uint2 y = tr4(tile, r1, col0);
+    return u32x4_t{x.x, x.y, y.x, y.y};
+  }
   // two K tiles (chunks c, c+1); at row start each wave stages its Q' in one
   static constexpr int kStageOff = 2 * kTile;
   static constexpr int kStageBytes = kSlots * 8;  // dI (fp32) + key (int32), ring of 4
@@ -257,7 +280,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
       u32x4_t o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = pack_bf16(wv * bf16_lo(v[e]), wv * bf16_hi(v[e]));
-      *reinterpret_cast<u32x4_t*>(qs + rotl5(l32) * L::kPitch + (8 * half + 16 * kd) * 2) = o;
+      *reinterpret_cast<u32x4_t*>(qs + L::at(rotl5(l32), (8 * half + 16 * kd) * 2)) = o;
     }
     wave_lds_sync();
     uint16_t* qtrow = P.qt + r * D * HP + 32 * g;
@@ -268,19 +291,20 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int ks = 0; ks < 2; ++ks) {
         const int r0 = 16 * ks + 8 * half;
         *reinterpret_cast<u32x4_t*>(qtrow + (32 * nd + l32) * HP + r0) =
-            lds_tr8(qs, L::kPitch, r0, r0 + 4, col0);
+            L::tr8(qs, r0, r0 + 4, col0);
       }
     }
     __syncthreads();  // both Q' tiles read before the K tiles take their place
   }
 
   // ---- chunk pipeline ---------------------------------------------------------
-  // Iteration c issues GEMM1 of chunk c+1 (K rows already in registers) before
-  // the VALU work of chunk c.  Slot data (dI, key) live in a ring of 4 stages
-  // written by the dI wave, the K rows of chunks c and c+1 in two LDS tiles
-  // of which each wave writes half the rows.  The barrier at the top of an
-  // iteration publishes both, and the record wave's view of wave 1's sign
-  // words of the previous chunk.
+  // Iteration c runs GEMM1 and GEMM2 of chunk c from its LDS tile, writes the
+  // K rows of chunk c+1 (gathered during iteration c-1) into the other tile
+  // and gathers those of chunk c+2; the gathers thus have a whole iteration to
+  // land.  Each wave gathers and writes half the rows of a tile.  Slot data
+  // (dI, key) live in a ring of 4 stages written by the dI wave.  The barrier
+  // at the top of an iteration publishes the tile and the stage, and the
+  // record wave's view of wave 1's sign words of the previous chunk.
   const int nchunks = (n + kSlots - 1) / kSlots;
   auto ktile = [&](int c) -> unsigned char* { return lds + (c & 1) * L::kTile; };
   auto stage_ptr = [&](int c) -> unsigned char* {
@@ -309,25 +333,37 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
     return key;
   };
-  // K rows in GEMM1's A layout: lane holds row l32, d = 8*half + 16*kd + e.
-  // Padding slots read row 0; their dI is 0, so they add nothing.
-  auto gather = [&](int key, u32x4_t (&kr)[KD]) {
-    const uint16_t* src = kb + int64_t(key < 0 ? 0 : key) * D + 8 * half;
+  // Each wave gathers only its RW rows of a chunk's K tile (all 32 when it is
+  // alone): lane L holds row grow = 16g + L % RW, 16-byte chunks
+  // L / RW + LPR*k.  Padding slots read row 0; their dI is 0, so they add
+  // nothing.  GEMM1 then reads its A operand (lane: row l32, d = 8*half +
+  // 16*kd + e) for all 32 rows from the shared tile.
+  constexpr int RW = kSlots / NG;   // K rows gathered by this wave
+  constexpr int LPR = 64 / RW;      // lanes per row
+  constexpr int NCH = D / 8 / LPR;  // 16-byte chunks per lane
+  const int grow = (NG == 2 ? 16 * g : 0) + lane % RW;
+  const int gch0 = lane / RW;
+  // key: the lane's slot key (lane l32 holds slot l32)
+  auto gather = [&](int key, u32x4_t (&kr)[NCH]) {
+    const int kr_key = __shfl(key, grow, 64);
+    const uint16_t* src = kb + int64_t(kr_key < 0 ? 0 : kr_key) * D;
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd) kr[kd] = *reinterpret_cast<const u32x4_t*>(src + 16 * kd);
+    for (int k = 0; k < NCH; ++k)
+      kr[k] = *reinterpret_cast<const u32x4_t*>(src + 8 * (gch0 + LPR * k));
   };
-  // this wave's rows of the K tile (all of them when it is alone)
-  auto store_ktile = [&](int c, const u32x4_t (&kr)[KD]) {
-    if (NG == 1 || (l32 >> 4) == g) {
+  auto store_ktile = [&](int c, const u32x4_t (&kr)[NCH]) {
 #pragma unroll
-      for (int kd = 0; kd < KD; ++kd)
-        *reinterpret_cast<u32x4_t*>(ktile(c) + l32 * L::kPitch + (8 * half + 16 * kd) * 2) = kr[kd];
-    }
+    for (int k = 0; k < NCH; ++k)
+      *reinterpret_cast<u32x4_t*>(ktile(c) + L::at(grow, (gch0 + LPR * k) * 16)) = kr[k];
   };
-  auto gemm1 = [&](const u32x4_t (&kr)[KD]) -> f32x16_t {
+  auto gemm1 = [&](int c) -> f32x16_t {
     f32x16_t s = f32x16_t{};
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd) s = mfma32(kr[kd], qb1[kd], s);
+    for (int kd = 0; kd < KD; ++kd) {
+      const u32x4_t a =
+          *reinterpret_cast<const u32x4_t*>(ktile(c) + L::at(l32, (8 * half + 16 * kd) * 2));
+      s = mfma32(a, qb1[kd], s);
+    }
     return s;
   };
 
@@ -352,22 +388,21 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
 
-  u32x4_t kr[KD];
+  u32x4_t kr[NCH];
   Raw raw;
-  f32x16_t sa = f32x16_t{}, sb = f32x16_t{};
   if (nchunks > 0) {
     gather(finalize(0, load_raw(0)), kr);
     raw = load_raw(1);
-    sa = gemm1(kr);
     store_ktile(0, kr);
     gather(finalize(1, raw), kr);
     raw = load_raw(2);
   }
 
-  // one pipeline step: chunk c with scores s_cur; GEMM1 of chunk c+1 -> s_next
-  auto step = [&](int c, const f32x16_t& s_cur, f32x16_t& s_next) {
+  // one pipeline step: chunk c (its K tile complete), the K rows of chunk c+1
+  // into the other tile, gathers of chunk c+2
+  auto step = [&](int c) {
     __syncthreads();  // K tile and stage of chunk c complete; chunk c-1 done by both waves
-    s_next = gemm1(kr);  // chunk c+1 (padding-only past the end)
+    const f32x16_t s_cur = gemm1(c);
     store_ktile(c + 1, kr);
     const int key_n2 = finalize(c + 2, raw);
     store_records(c - 1);
@@ -419,7 +454,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int nd = 0; nd < ND; ++nd) {
         const int col0 = 32 * nd + 16 * ((lane >> 4) & 1);
         const int r0 = 16 * ks + 4 * half;
-        dqacc[nd] = mfma32(aop, lds_tr8(ktile(c), L::kPitch, r0, r0 + 8, col0), dqacc[nd]);
+        dqacc[nd] = mfma32(aop, L::tr8(ktile(c), r0, r0 + 8, col0), dqacc[nd]);
       }
     }
 
@@ -446,11 +481,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
       prev_mask = maskword;
     }
   };
-  // unrolled by two: the score tiles alternate without register copies
-  for (int c = 0; c < nchunks; c += 2) {
-    step(c, sa, sb);
-    if (c + 1 < nchunks) step(c + 1, sb, sa);
-  }
+  for (int c = 0; c < nchunks; ++c) step(c);
   __syncthreads();  // the last chunk's sign words of wave 1
   store_records(nchunks - 1);
 
