@@ -101,8 +101,8 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_bal
 // keeps a running max and a sum rescaled to it, then the wave combines them.
 // c2*I is rounded before any max is subtracted (no contraction into a
 // multiply-add), so the largest logit contributes 2^0 = 1 exactly.
-// on_group(key) is called by every lane, in uniform control flow, once per
-// slot position j0 + 64u + lane (key < 0 for padding and positions past n).
+// on_group(j, key) is called by every lane, in uniform control flow, once per
+// slot position j = j0 + 64u + lane (key < 0 for padding and positions past n).
 // Both row kernels use this and slot_dI, so their dI agree bit for bit.
 template <typename IdAt, typename KeyOf, typename OnGroup>
 __device__ __forceinline__ float2 row_softmax_stats(int n, const float* __restrict__ Irow, float c2,
@@ -130,7 +130,7 @@ __device__ __forceinline__ float2 row_softmax_stats(int n, const float* __restri
         z = z * __builtin_amdgcn_exp2f(m2 - mn) + __builtin_amdgcn_exp2f(v - mn);
         m2 = mn;
       }
-      if (j0 + 64 * u < n) on_group(key);
+      if (j0 + 64 * u < n) on_group(j0 + 64 * u + lane, key);
     }
   }
   const float mw = wave_max(m2);

@@ -37,7 +37,7 @@ void stage_done(int stage, const char* kernel) {
 
 hipError_t launch(Problem P, void* workspace, hipStream_t stream) {
   hipError_t err;
-  const Layout L = make_layout(P.B, P.S_q, P.S_k, P.H, P.D, P.row_len);
+  const Layout L = make_layout(P.B, P.S_q, P.S_k, P.H, P.D, P.row_len, P.dense);
   P.rec_stride = L.rec_stride;
   P.RK = L.RK;
   P.NR = L.NR;
@@ -58,6 +58,7 @@ hipError_t launch(Problem P, void* workspace, hipStream_t stream) {
   P.rkd = reinterpret_cast<int*>(ws + L.off_rkd);
   P.rmask = reinterpret_cast<uint32_t*>(ws + L.off_rmask);
   P.offs = reinterpret_cast<int*>(ws + L.off_offs);
+  P.rank = reinterpret_cast<int*>(ws + L.off_rank);
   P.qt = reinterpret_cast<uint16_t*>(ws + L.off_qt);
   P.slab = reinterpret_cast<float*>(ws + L.off_slab);
   if ((err = launch_rows_export(P, stream)) != hipSuccess) return err;

@@ -73,7 +73,7 @@ struct ExportLds {
   }
   // two K tiles (chunks c, c+1); at row start each wave stages its Q' in one
   static constexpr int kStageOff = 2 * kTile;
-  static constexpr int kStageBytes = kSlots * 8;  // dI (fp32) + key (int32), ring of 4
+  static constexpr int kStageBytes = kSlots * 12;  // dI (fp32), key, record position; ring of 4
   static constexpr int kW1Off = kStageOff + 4 * kStageBytes;  // sign words of wave 1, ring of 2
   static constexpr int kStatOff = kW1Off + 2 * kSlots * 4;    // m2, invZ
   static constexpr int kCursorOff = kStatOff + 16;
@@ -94,6 +94,7 @@ struct Raw {
   int id;
   float I;
   float p;
+  int rank;
 };
 
 __device__ __forceinline__ int rotl5(int b) { return ((b << 1) | (b >> 4)) & 31; }
@@ -107,6 +108,22 @@ __device__ __forceinline__ uint64_t same_range_lanes(bool valid, int r, int nbit
     same &= ((r >> b) & 1) ? bb : ~bb;
   }
   return same;
+}
+
+// Counting pass over one group of 64 slots (slot j of this lane, key < 0 for
+// padding): the range counts in cursor[] grow by the group's slots, and each
+// valid slot's rank among the row's earlier slots of its range goes to
+// rank_row[j].
+__device__ __forceinline__ void count_and_rank(int* cursor, int* rank_row, int j, int key, int RK,
+                                               int nbits) {
+  const bool valid = key >= 0;
+  const int rg = valid ? key / RK : 0;
+  const uint64_t same = same_range_lanes(valid, rg, nbits);
+  const int base = valid ? cursor[rg] : 0;
+  wave_lds_sync();
+  if (valid && (same & lanemask_lt()) == 0) cursor[rg] = base + __popcll(same);
+  wave_lds_sync();
+  if (valid) rank_row[j] = base + __popcll(same & lanemask_lt());
 }
 
 template <int D, bool DENSE, int NG>
@@ -142,6 +159,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   const float* Irow = P.I + r * P.row_len;
   const float* prow = P.p + r * P.row_len;
   const int32_t* idrow = DENSE ? nullptr : P.ids + r * P.row_len;
+  int* rank_row = DENSE ? nullptr : P.rank + r * P.row_len;
   const uint16_t* kb = P.k + b * P.S_k * D;
   const int S_k = int(P.S_k);
   constexpr int RK = kRangeKeys;  // power of two: divisions are shifts
@@ -160,23 +178,18 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   const float c2 = P.sm_scale * 1.4426950408889634f;  // base-2 logit scale
   const float coef = P.grad_loss * P.sm_scale;
 
-  // ---- record wave: slot count of every key range (ballots, no LDS atomics:
-  //      gfx950 runs those at about 190 cycles per instruction for the CU);
-  //      dI wave: softmax statistics.  One pass over the row each. -------------
+  // ---- record wave: slot count of every key range and rank of every slot
+  //      within its range (ballots, no LDS atomics: gfx950 runs those at about
+  //      190 cycles per instruction for the CU); dI wave: softmax statistics.
+  //      One pass over the row each. -------------------------------------------
   if (rec_wave && !DENSE) {
     for (int i = lane; i < NR; i += 64) cursor[i] = 0;
     wave_lds_sync();
   }
   if (dI_wave) {
     const float2 st = row_softmax_stats(
-        n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [&](int key) {
-          if (NG == 1 && !DENSE) {
-            const bool valid = key >= 0;
-            const int rg = valid ? key / RK : 0;
-            const uint64_t same = same_range_lanes(valid, rg, nbits);
-            if (valid && (same & lanemask_lt()) == 0) cursor[rg] += __popcll(same);
-            wave_lds_sync();
-          }
+        n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [&](int j, int key) {
+          if (NG == 1 && !DENSE) count_and_rank(cursor, rank_row, j, key, RK, nbits);
         });
     if (lane == 0) {
       stat[0] = st.x;
@@ -195,12 +208,8 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         if (j0 + 64 * u < n) {
-          const int key = key_of(j0 + 64 * u + lane, idv[u]);
-          const bool valid = key >= 0;
-          const int rg = valid ? key / RK : 0;
-          const uint64_t same = same_range_lanes(valid, rg, nbits);
-          if (valid && (same & lanemask_lt()) == 0) cursor[rg] += __popcll(same);
-          wave_lds_sync();
+          const int j = j0 + 64 * u + lane;
+          count_and_rank(cursor, rank_row, j, key_of(j, idv[u]), RK, nbits);
         }
       }
     }
@@ -316,13 +325,15 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int jc = j < row_len ? j : row_len - 1;
     Raw v;
     v.id = DENSE ? 0 : idrow[jc];
-    // the record wave of a pair needs only the ids
+    // the record wave of a pair needs only the ids and ranks
     v.I = dI_wave ? Irow[jc] : 0.f;
     v.p = dI_wave ? prow[jc] : 0.f;
+    v.rank = rec_wave && !DENSE ? rank_row[jc] : 0;
     return v;
   };
-  // key of the lane's slot; the dI wave also publishes dI and key (lanes l and
-  // l+32 write the same values)
+  // key of the lane's slot; the dI wave also publishes dI and key, the record
+  // wave the position of the slot's record: its range's start plus its rank
+  // (lanes l and l+32 write the same values)
   auto finalize = [&](int c, const Raw& v) -> int {
     const int j = c * kSlots + l32;
     const int key = key_of(j, v.id);
@@ -330,6 +341,11 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
       const float dI = key >= 0 ? slot_dI(v.I, v.p, c2, m2, invZ, coef) : 0.f;
       reinterpret_cast<float*>(stage_ptr(c))[l32] = dI;
       reinterpret_cast<int*>(stage_ptr(c) + kSlots * 4)[l32] = key;
+    }
+    if (rec_wave) {
+      int pos = 0;
+      if (key >= 0) pos = DENSE ? j + kSinks * (j / RK) : cursor[key / RK] + v.rank;
+      reinterpret_cast<int*>(stage_ptr(c) + kSlots * 8)[l32] = pos;
     }
     return key;
   };
@@ -458,24 +474,11 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     }
 
-    // ---- record wave: position of every valid slot's record: range start +
-    //      earlier slots of the same range (slot order) -------------------------
+    // ---- record wave: this chunk's records, stored in the next iteration -----
     if (rec_wave) {
       const int key = sk[l32];
       const bool valid = lane < kSlots && key >= 0;
-      int pos;
-      if (DENSE) {
-        const int j = c * kSlots + l32;
-        pos = j + kSinks * (j / RK);
-      } else {
-        const int rg = valid ? key / RK : 0;
-        const uint64_t same = same_range_lanes(valid, rg, nbits);
-        const int base = valid ? cursor[rg] : 0;
-        pos = base + __popcll(same & lanemask_lt());
-        wave_lds_sync();
-        if (valid && (same & lanemask_lt()) == 0) cursor[rg] = base + __popcll(same);
-      }
-      prev_pos = pos;
+      prev_pos = reinterpret_cast<const int*>(stage_ptr(c) + kSlots * 8)[l32];
       prev_valid = valid;
       prev_kd = make_int2(key, __float_as_int(sd[l32]));
       prev_mask = maskword;

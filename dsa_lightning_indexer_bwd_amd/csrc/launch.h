@@ -31,19 +31,21 @@ enum DkRoute : int {
 //   rmask [rows][rec_stride][2] u32 sign bits [S > 0] of heads 0..31, 32..63
 //         (bit b of word g is head 32g + rotl5(b), rotl5 = 5-bit rotate left)
 //   offs  [rows][NR] int2           {first, end} record of each range
+//   rank  [rows][row_len] int32     rank of each valid slot among the row's
+//                                   slots of its range (sparse rows only)
 //   qt    [rows][D][HP] bf16        (w*q)^T of every row, heads padded to HP
 //   slab  [B][NQB][NR*RK][D] fp32   per query block partial dK
 // rec_stride = row_len + 36*NR (sinks and alignment) + 32 (stores of padding
 // lanes), rounded up to a multiple of 4.
 struct Layout {
   int64_t rows, row_len, rec_stride, HP, RK, NR, NQB, QBS, nchunk;
-  size_t off_rkd, off_rmask, off_offs, off_qt, off_slab, total;
+  size_t off_rkd, off_rmask, off_offs, off_rank, off_qt, off_slab, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
-                          int64_t row_len) {
+                          int64_t row_len, bool dense) {
   Layout L{};
   L.rows = B * S_q;
   L.row_len = row_len;
@@ -70,6 +72,8 @@ inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_
   o = align256(o + recs * 8 + kRecBlock * 8);
   L.off_offs = o;
   o = align256(o + size_t(L.rows) * size_t(L.NR) * 8);
+  L.off_rank = o;
+  if (!dense) o = align256(o + size_t(L.rows) * size_t(row_len) * 4);
   L.off_qt = o;
   o = align256(o + size_t(L.rows) * size_t(D) * size_t(L.HP) * 2);
   L.off_slab = o;
@@ -99,6 +103,7 @@ struct Problem {
   int* rkd;  // int2 pairs {key, dI bits}
   uint32_t* rmask;
   int* offs;  // int2 pairs
+  int* rank;
   uint16_t* qt;
   float* slab;
   int64_t rec_stride, RK, NR, NQB, QBS, nchunk, HP;
