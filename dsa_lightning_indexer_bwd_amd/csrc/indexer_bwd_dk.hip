@@ -394,11 +394,15 @@ dk_range_kernel(Problem P) {
       // intact until the scatter of query qi+2, one iteration later)
       const int kq[2] = {key[0], key[1]};
       // table of query qi+1: its last readers finished query qi-1
+      // the MMA waves wait for this table at the next barrier: the producer's
+      // work of the iteration runs at the highest priority of the CU's waves
+      __builtin_amdgcn_s_setprio(2);
       if (qi + 1 < nne) scatter(e1, (qi + 1) & 3, (qi + 1) & 1, qi + 1, key);
       dup = dup || lost_any(n, kq, qi & 1, qi);
       // stage (qi+3) % 4 = (qi-1) % 4 was last read by the scatter of query
       // qi-1, whose table writes waited for those reads
       if (qi + 3 < nne) dma_recs(uni(e3.x), uni(e3.y), (qi + 3) & 3);
+      __builtin_amdgcn_s_setprio(0);
     }
   } else {
     auto wait_prev = [&](bool issued) {
@@ -423,7 +427,11 @@ dk_range_kernel(Problem P) {
       const int r2 = row2;
       if (qi + 3 < nne) row2 = list[qi + 3].x;
       if (qi + 2 < nne) dma_qt(r2, q2);
+      // raised priority while this wave expands and issues its MFMAs, so that
+      // the other MMA wave of the SIMD fills the gaps with its own work
+      __builtin_amdgcn_s_setprio(1);
       mfma_pass(qi & 1, q0, qi);
+      __builtin_amdgcn_s_setprio(0);
       q0 = q0 == 2 ? 0 : q0 + 1;
       q2 = q2 == 2 ? 0 : q2 + 1;
     }

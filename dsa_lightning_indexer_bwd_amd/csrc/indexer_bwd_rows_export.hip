@@ -418,7 +418,11 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   // into the other tile, gathers of chunk c+2
   auto step = [&](int c) {
     __syncthreads();  // K tile and stage of chunk c complete; chunk c-1 done by both waves
+    // raised priority while this wave issues its MFMAs, so that the other wave
+    // of the SIMD fills the gaps with its VALU work
+    __builtin_amdgcn_s_setprio(1);
     const f32x16_t s_cur = gemm1(c);
+    __builtin_amdgcn_s_setprio(0);
     store_ktile(c + 1, kr);
     const int key_n2 = finalize(c + 2, raw);
     store_records(c - 1);
@@ -463,6 +467,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     // ---- GEMM2: dQ'[h][d] += G'[h][j] K[j][d] ----------------------------------
     // k-step ks covers slots 16*ks + {0..15}; register e of lane (half) is slot
     // 16*ks + 8*(e/4) + 4*half + e%4 (GEMM1's output order)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4_t aop = u32x4_t{gp[2 * ks][0], gp[2 * ks][1], gp[2 * ks + 1][0], gp[2 * ks + 1][1]};
@@ -473,6 +478,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
         dqacc[nd] = mfma32(aop, L::tr8(ktile(c), r0, r0 + 8, col0), dqacc[nd]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- record wave: this chunk's records, stored in the next iteration -----
     if (rec_wave) {
