@@ -211,10 +211,14 @@ def kernel_model(name, wl, B, H, D, S_q, S_k):
     """(bound, algorithmic work per launch) of one kernel of the call.
 
     Work units per query row are the row's slots (topk, or t+1 for the dense
-    variant): the row kernels do GEMM1 + GEMM2 (4*H*D FLOP per slot), the range
+    variant): the prep kernel reads the slot inputs and writes one 8-byte
+    {position, dI} per slot, the row kernels do GEMM1 + GEMM2 (4*H*D FLOP per slot), the range
     kernel the dK GEMM (2*H*D per slot), the atomic-route row kernel all three.
     The slab sum reads every query block's partial dK once and writes d_k."""
     slots = wl.flops() // (6 * H * D)
+    if name == "row_prep_kernel":
+        # ids (sparse), I and p read once, {position, dI} written per slot
+        return "hbm", (16 if wl.dense else 20) * slots
     if name == "row_export_kernel":
         return "mfma", 4 * H * D * slots
     if name == "dk_range_kernel":

@@ -74,6 +74,13 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The same ordering for the compiler only.  A wavefront-scope fence also
+// waits for every outstanding global memory operation of the wave (gfx9
+// counts loads and stores in one counter); lanes that exchange data through
+// LDS within one wave need just the issue order, which this keeps, so loads
+// in flight and stores just issued are not waited for.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;

@@ -64,9 +64,9 @@ int check_common(const void* q, const void* k, const float* w, const float* I, c
 }
 
 size_t workspace_bytes(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
-                       int64_t row_len, bool dense, uint32_t flags) {
+                       int64_t row_len, uint32_t flags) {
   if (flags & IBWD_FLAG_ATOMIC_DK) return 0;
-  return ibwd::make_layout(B, S_q, S_k, H, D, row_len, dense).total;
+  return ibwd::make_layout(B, S_q, S_k, H, D, row_len).total;
 }
 
 }  // namespace
@@ -82,7 +82,7 @@ int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32
                         flags);
   if (st != IBWD_OK) return st;
   if (!topk_ids || !aligned(topk_ids, 4)) return IBWD_ERR_INVALID_ARGUMENT;
-  size_t need = workspace_bytes(B, S_q, S_k, H, D, topk, false, flags);
+  size_t need = workspace_bytes(B, S_q, S_k, H, D, topk, flags);
   if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256)))
     return IBWD_ERR_INVALID_ARGUMENT;
   st = device_status();
@@ -121,7 +121,7 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
   if (st != IBWD_OK) return st;
   if (q_offset < -(int64_t(1) << 40) || q_offset > (int64_t(1) << 40))
     return IBWD_ERR_INVALID_ARGUMENT;
-  size_t need = workspace_bytes(B, S_q, S_k, H, D, S_k, true, flags);
+  size_t need = workspace_bytes(B, S_q, S_k, H, D, S_k, flags);
   if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256)))
     return IBWD_ERR_INVALID_ARGUMENT;
   st = device_status();
@@ -156,7 +156,7 @@ size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_
   if (B < 1 || S_q < 1 || S_k < 1 || H < 1 || H > ibwd::kMaxHeads || row_len < 1) return 0;
   if (D != 32 && D != 64 && D != 128) return 0;
   if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, row_len)) return 0;
-  return workspace_bytes(B, S_q, S_k, H, D, row_len, dense != 0, flags);
+  return workspace_bytes(B, S_q, S_k, H, D, row_len, flags);
 }
 
 const char* indexer_bwd_strerror(int status) {

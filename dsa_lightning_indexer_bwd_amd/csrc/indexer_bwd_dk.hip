@@ -541,13 +541,13 @@ hipError_t launch_dk_t(const Problem& P, hipStream_t stream) {
   if (err != hipSuccess) return err;
   dk_range_kernel<NH, D><<<grid, S::NTH, S::kBytes, stream>>>(P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  stage_done(1, "dk_range_kernel");
+  stage_done(2, "dk_range_kernel");
   const int64_t n4 = P.B * P.S_k * P.D / 4;
   int64_t blocks = (n4 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   dk_sum_kernel<<<unsigned(blocks), 256, 0, stream>>>(P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  stage_done(2, "dk_sum_kernel");
+  stage_done(3, "dk_sum_kernel");
   return hipSuccess;
 }
 

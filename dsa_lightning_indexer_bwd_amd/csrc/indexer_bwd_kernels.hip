@@ -1,6 +1,8 @@
 // Launch sequence of the lightning-indexer backward on gfx950.
 //
 //   two-pass route (default, bitwise deterministic):
+//     row_prep_kernel   one wave per query row: softmax statistics, record
+//                       layout by key range, per-slot record position and dI
 //     row_export_kernel one wave per (query row, 32 heads): dQ, dW, slot records
 //                     (key, dI, sign mask of S over h), (w*q)^T
 //     dk_range_kernel one workgroup per (key range, query block): dK slabs in LDS
@@ -37,7 +39,7 @@ void stage_done(int stage, const char* kernel) {
 
 hipError_t launch(Problem P, void* workspace, hipStream_t stream) {
   hipError_t err;
-  const Layout L = make_layout(P.B, P.S_q, P.S_k, P.H, P.D, P.row_len, P.dense);
+  const Layout L = make_layout(P.B, P.S_q, P.S_k, P.H, P.D, P.row_len);
   P.rec_stride = L.rec_stride;
   P.RK = L.RK;
   P.NR = L.NR;
@@ -58,12 +60,11 @@ hipError_t launch(Problem P, void* workspace, hipStream_t stream) {
   P.rkd = reinterpret_cast<int*>(ws + L.off_rkd);
   P.rmask = reinterpret_cast<uint32_t*>(ws + L.off_rmask);
   P.offs = reinterpret_cast<int*>(ws + L.off_offs);
-  P.rank = reinterpret_cast<int*>(ws + L.off_rank);
+  P.slot = reinterpret_cast<int*>(ws + L.off_slot);
   P.qt = reinterpret_cast<uint16_t*>(ws + L.off_qt);
   P.slab = reinterpret_cast<float*>(ws + L.off_slab);
-  if ((err = launch_rows_export(P, stream)) != hipSuccess) return err;
-  stage_done(0, "row_export_kernel");
-  return launch_dk(P, stream);  // reports stages 1 and 2
+  if ((err = launch_rows_export(P, stream)) != hipSuccess) return err;  // stages 0, 1
+  return launch_dk(P, stream);  // stages 2, 3
 }
 
 }  // namespace ibwd

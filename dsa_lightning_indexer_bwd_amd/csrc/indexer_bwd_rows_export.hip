@@ -16,11 +16,14 @@
 // workgroup).  Each wave then needs half the registers (dQ' accumulators, Q,
 // the score tile), so it fits in 256 registers and two waves share each SIMD:
 // one wave's VALU work (mask, G', dW) overlaps the other's MFMA work.  The
-// per-row work that does not depend on the heads is split between the two
-// waves instead of repeated: wave 1 computes the softmax statistics and dI,
-// wave 0 counts and ranks the slots by key range and stores the records; each
-// wave stores half the rows of the shared K tile.  One barrier per chunk.
-// With H <= 32 a single wave does all of it.
+// softmax statistics, the record layout and every slot's dI and record
+// position come from a prep kernel that runs first (one wave per row, many
+// rows in flight per CU, so its dependent global round trips overlap across
+// rows instead of stalling the MFMA work of this kernel).  The per-slot work
+// that does not depend on the heads is split between the two waves instead of
+// repeated: wave 1 stages dI and key, wave 0 the record position and stores
+// the records; each wave gathers and stores half the rows of the shared K
+// tile.  One barrier per chunk.  With H <= 32 a single wave does all of it.
 //
 // Per chunk of 32 slots:
 //   GEMM1  S^T[j,h]  = K_g[j,:] . Q[h,:]     v_mfma 32x32x16, M=j N=h K=d; K_g
@@ -75,26 +78,12 @@ struct ExportLds {
   static constexpr int kStageOff = 2 * kTile;
   static constexpr int kStageBytes = kSlots * 12;  // dI (fp32), key, record position; ring of 4
   static constexpr int kW1Off = kStageOff + 4 * kStageBytes;  // sign words of wave 1, ring of 2
-  static constexpr int kStatOff = kW1Off + 2 * kSlots * 4;    // m2, invZ
-  static constexpr int kCursorOff = kStatOff + 16;
-  // The range scan keeps one end offset per range in a scratch array that
-  // lives in the K tiles while they are unused, or past the cursor when it
-  // does not fit there (small D with many ranges).
-  __host__ __device__ static int ends_off(int64_t NR) {
-    return NR * 4 <= kStageOff ? 0 : kCursorOff + int(NR) * 4;
-  }
-  // dynamic size: the cursor holds one int per key range of the problem
-  static size_t bytes(int64_t NR) {
-    const size_t cur = size_t(kCursorOff) + size_t(NR) * 4;
-    return ends_off(NR) == 0 ? cur : cur + size_t(NR) * 4;
-  }
+  static constexpr int kBytes = kW1Off + 2 * kSlots * 4;
 };
 
 struct Raw {
   int id;
-  float I;
-  float p;
-  int rank;
+  int2 pd;  // {record position (-1: padding), dI bits} from the prep kernel
 };
 
 __device__ __forceinline__ int rotl5(int b) { return ((b << 1) | (b >> 4)) & 31; }
@@ -110,20 +99,127 @@ __device__ __forceinline__ uint64_t same_range_lanes(bool valid, int r, int nbit
   return same;
 }
 
-// Counting pass over one group of 64 slots (slot j of this lane, key < 0 for
-// padding): the range counts in cursor[] grow by the group's slots, and each
-// valid slot's rank among the row's earlier slots of its range goes to
-// rank_row[j].
-__device__ __forceinline__ void count_and_rank(int* cursor, int* rank_row, int j, int key, int RK,
-                                               int nbits) {
-  const bool valid = key >= 0;
-  const int rg = valid ? key / RK : 0;
-  const uint64_t same = same_range_lanes(valid, rg, nbits);
-  const int base = valid ? cursor[rg] : 0;
-  wave_lds_sync();
-  if (valid && (same & lanemask_lt()) == 0) cursor[rg] = base + __popcll(same);
-  wave_lds_sync();
-  if (valid) rank_row[j] = base + __popcll(same & lanemask_lt());
+// Per query row, before the row kernel: the softmax statistics over the valid
+// slots, the slot count of every 128-key range, the row's record layout
+// (ranges in key order, each starting at a multiple of 4 entries, slots in
+// slot order within a range) and, for every slot, its record position and its
+// dI.  One wave per row and no MFMA work, so many rows are in flight per CU and
+// the dependent global round trips of these passes overlap across rows.
+//   pass 1: statistics and range counts (ballots of the range bits; no LDS
+//           atomics: gfx950 runs those at about 190 cycles per instruction for
+//           the CU)
+//   scan:   range starts; {first, end} of every range to `offs`
+//   pass 2: positions (range start + earlier slots of the range, from the
+//           same ballots) and dI, as {position or -1, dI} per slot
+template <bool DENSE>
+__global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
+  extern __shared__ int cursor[];  // one int per key range
+  const int lane = threadIdx.x;
+  const int64_t r = int64_t(blockIdx.x);
+  const int64_t t = r % P.S_q;
+  const int row_len = int(P.row_len);
+  int n = row_len;
+  if (DENSE) {
+    const int64_t last = t + P.q_offset;
+    n = last < 0 ? 0 : int(last + 1 < P.S_k ? last + 1 : P.S_k);
+  }
+  const float* Irow = P.I + r * P.row_len;
+  const float* prow = P.p + r * P.row_len;
+  const int32_t* idrow = DENSE ? nullptr : P.ids + r * P.row_len;
+  int2* slot = reinterpret_cast<int2*>(P.slot) + r * P.row_len;
+  int2* offrow = reinterpret_cast<int2*>(P.offs) + r * P.NR;
+  const int S_k = int(P.S_k);
+  constexpr int RK = kRangeKeys;  // power of two: divisions are shifts
+  const int NR = int(P.NR);
+  auto key_of = [&](int j, int id) -> int {
+    if (j >= n) return -1;
+    if (DENSE) return j;
+    return (id >= 0 && id < S_k) ? id : -1;
+  };
+  int nbits = 0;
+  while ((1 << nbits) < NR) ++nbits;
+  const float c2 = P.sm_scale * 1.4426950408889634f;  // base-2 logit scale
+  const float coef = P.grad_loss * P.sm_scale;
+
+  // ---- pass 1: statistics, range counts ----------------------------------------
+  if (!DENSE) {
+    for (int i = lane; i < NR; i += 64) cursor[i] = 0;
+    lds_order();
+  }
+  const float2 st = row_softmax_stats(
+      n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [&](int, int key) {
+        if (!DENSE) {
+          const bool valid = key >= 0;
+          const int rg = valid ? key / RK : 0;
+          const uint64_t same = same_range_lanes(valid, rg, nbits);
+          if (valid && (same & lanemask_lt()) == 0) cursor[rg] += __popcll(same);
+          lds_order();
+        }
+      });
+
+  // ---- range starts and {first, end} -------------------------------------------
+  if (DENSE) {
+    // record of slot j at j: ranges are already in key order, 128 apart
+    for (int i = lane; i < NR; i += 64) {
+      const int cnt = n - i * RK < 0 ? 0 : (n - i * RK < RK ? n - i * RK : RK);
+      offrow[i] = cnt > 0 ? make_int2(i * RK, i * RK + cnt) : make_int2(0, 0);
+    }
+  } else {
+    const int per = (NR + 63) / 64;
+    const int s0 = lane * per < NR ? lane * per : NR;
+    const int s1 = s0 + per < NR ? s0 + per : NR;
+    int sum = 0;
+    for (int i = s0; i < s1; ++i) sum += (cursor[i] + 3) & ~3;
+    int incl = sum;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - sum;
+    lds_order();
+    for (int i = s0; i < s1; ++i) {
+      const int cnt = cursor[i];
+      cursor[i] = run;
+      offrow[i] = make_int2(run, run + cnt);
+      run += (cnt + 3) & ~3;
+    }
+    lds_order();
+  }
+
+  // ---- pass 2: record position and dI of every slot ------------------------------
+  constexpr int kU = 4;  // loads in flight per lane and array
+  for (int j0 = 0; j0 < n; j0 += 64 * kU) {
+    int idv[kU];
+    float iv[kU], pv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + 64 * u + lane;
+      const int jc = j < n ? j : n - 1;
+      idv[u] = DENSE ? 0 : idrow[jc];
+      iv[u] = Irow[jc];
+      pv[u] = prow[jc];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (j0 + 64 * u < n) {
+        const int j = j0 + 64 * u + lane;
+        const int key = key_of(j, idv[u]);
+        const bool valid = key >= 0;
+        int pos = j;
+        if (!DENSE) {
+          const int rg = valid ? key / RK : 0;
+          const uint64_t same = same_range_lanes(valid, rg, nbits);
+          const int base = valid ? cursor[rg] : 0;
+          pos = base + __popcll(same & lanemask_lt());
+          lds_order();
+          if (valid && (same & lanemask_lt()) == 0) cursor[rg] = base + __popcll(same);
+          lds_order();
+        }
+        const float dI = valid ? slot_dI(iv[u], pv[u], c2, st.x, st.y, coef) : 0.f;
+        if (j < n) slot[j] = make_int2(valid ? pos : -1, __float_as_int(dI));
+      }
+    }
+  }
 }
 
 template <int D, bool DENSE, int NG>
@@ -156,117 +252,18 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int64_t last = t + P.q_offset;
     n = last < 0 ? 0 : int(last + 1 < P.S_k ? last + 1 : P.S_k);
   }
-  const float* Irow = P.I + r * P.row_len;
-  const float* prow = P.p + r * P.row_len;
   const int32_t* idrow = DENSE ? nullptr : P.ids + r * P.row_len;
-  int* rank_row = DENSE ? nullptr : P.rank + r * P.row_len;
+  const int2* slotrow = reinterpret_cast<const int2*>(P.slot) + r * P.row_len;
   const uint16_t* kb = P.k + b * P.S_k * D;
   const int S_k = int(P.S_k);
-  constexpr int RK = kRangeKeys;  // power of two: divisions are shifts
-  const int NR = int(P.NR);
-  int* cursor = reinterpret_cast<int*>(lds + L::kCursorOff);
-  float* stat = reinterpret_cast<float*>(lds + L::kStatOff);
 
   auto key_of = [&](int j, int id) -> int {
     if (j >= n) return -1;
     if (DENSE) return j;
     return (id >= 0 && id < S_k) ? id : -1;
   };
-
-  int nbits = 0;
-  while ((1 << nbits) < NR) ++nbits;
-  const float c2 = P.sm_scale * 1.4426950408889634f;  // base-2 logit scale
-  const float coef = P.grad_loss * P.sm_scale;
-
-  // ---- record wave: slot count of every key range and rank of every slot
-  //      within its range (ballots, no LDS atomics: gfx950 runs those at about
-  //      190 cycles per instruction for the CU); dI wave: softmax statistics.
-  //      One pass over the row each. -------------------------------------------
-  if (rec_wave && !DENSE) {
-    for (int i = lane; i < NR; i += 64) cursor[i] = 0;
-    wave_lds_sync();
-  }
-  if (dI_wave) {
-    const float2 st = row_softmax_stats(
-        n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [&](int j, int key) {
-          if (NG == 1 && !DENSE) count_and_rank(cursor, rank_row, j, key, RK, nbits);
-        });
-    if (lane == 0) {
-      stat[0] = st.x;
-      stat[1] = st.y;
-    }
-  } else if (!DENSE) {
-    // record wave of a pair: the counts only
-    constexpr int kU = 8;
-    for (int j0 = 0; j0 < n; j0 += 64 * kU) {
-      int idv[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int j = j0 + 64 * u + lane;
-        idv[u] = idrow[j < n ? j : n - 1];
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (j0 + 64 * u < n) {
-          const int j = j0 + 64 * u + lane;
-          count_and_rank(cursor, rank_row, j, key_of(j, idv[u]), RK, nbits);
-        }
-      }
-    }
-  }
-
-  // ---- record wave: range table: range i holds [first_i, end_i), then kSinks
-  //      sink entries with key (i+1)*RK; ranges start at multiples of 4 -------
-  int2* offrow = reinterpret_cast<int2*>(P.offs) + r * P.NR;
   int2* rkd = reinterpret_cast<int2*>(P.rkd) + r * P.rec_stride;
   uint2* rmask = reinterpret_cast<uint2*>(P.rmask) + r * P.rec_stride;
-  if (rec_wave) {
-    if (DENSE) {
-      // record of slot j at j + kSinks*(j / RK): ranges are already in key order
-      const int nr_used = (n + RK - 1) / RK;
-      for (int i = lane; i < NR; i += 64) {
-        const int cnt = n - i * RK < 0 ? 0 : (n - i * RK < RK ? n - i * RK : RK);
-        const int first = i * (RK + kSinks);
-        offrow[i] = cnt > 0 ? make_int2(first, first + cnt) : make_int2(0, 0);
-      }
-      for (int i0 = 0; i0 < nr_used; i0 += 2) {
-        const int i = i0 + half;
-        if (i < nr_used) {
-          const int cnt = n - i * RK < RK ? n - i * RK : RK;
-          rkd[i * (RK + kSinks) + cnt + l32] = make_int2((i + 1) * RK, 0);
-        }
-      }
-    } else {
-      wave_lds_sync();
-      int* ends = reinterpret_cast<int*>(lds + L::ends_off(NR));  // free until Q' is staged
-      const int per = (NR + 63) / 64;
-      const int s0 = lane * per < NR ? lane * per : NR;
-      const int s1 = s0 + per < NR ? s0 + per : NR;
-      int sum = 0;
-      for (int i = s0; i < s1; ++i) sum += (cursor[i] + kSinks + 3) & ~3;
-      int incl = sum;
-      for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-      }
-      int run = incl - sum;
-      wave_lds_sync();
-      for (int i = s0; i < s1; ++i) {
-        const int cnt = cursor[i];
-        cursor[i] = run;
-        ends[i] = run + cnt;
-        offrow[i] = make_int2(run, run + cnt);
-        run += (cnt + kSinks + 3) & ~3;
-      }
-      wave_lds_sync();
-      for (int i0 = 0; i0 < NR; i0 += 2) {
-        const int i = i0 + half;
-        if (i < NR) rkd[ends[i] + l32] = make_int2((i + 1) * RK, 0);
-      }
-    }
-  }
-  __syncthreads();  // statistics published; the ends scratch is free again
-  const float m2 = stat[0], invZ = stat[1];
 
   // ---- per-row operands: this wave's heads -----------------------------------
   const int hl = 32 * g + rotl5(l32);  // head of lane l32 in GEMM1's N dimension
@@ -325,28 +322,20 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int jc = j < row_len ? j : row_len - 1;
     Raw v;
     v.id = DENSE ? 0 : idrow[jc];
-    // the record wave of a pair needs only the ids and ranks
-    v.I = dI_wave ? Irow[jc] : 0.f;
-    v.p = dI_wave ? prow[jc] : 0.f;
-    v.rank = rec_wave && !DENSE ? rank_row[jc] : 0;
+    v.pd = slotrow[jc];
     return v;
   };
   // key of the lane's slot; the dI wave also publishes dI and key, the record
-  // wave the position of the slot's record: its range's start plus its rank
-  // (lanes l and l+32 write the same values)
+  // wave the position of the slot's record (lanes l and l+32 write the same
+  // values)
   auto finalize = [&](int c, const Raw& v) -> int {
     const int j = c * kSlots + l32;
     const int key = key_of(j, v.id);
     if (dI_wave) {
-      const float dI = key >= 0 ? slot_dI(v.I, v.p, c2, m2, invZ, coef) : 0.f;
-      reinterpret_cast<float*>(stage_ptr(c))[l32] = dI;
+      reinterpret_cast<float*>(stage_ptr(c))[l32] = key >= 0 ? __int_as_float(v.pd.y) : 0.f;
       reinterpret_cast<int*>(stage_ptr(c) + kSlots * 4)[l32] = key;
     }
-    if (rec_wave) {
-      int pos = 0;
-      if (key >= 0) pos = DENSE ? j + kSinks * (j / RK) : cursor[key / RK] + v.rank;
-      reinterpret_cast<int*>(stage_ptr(c) + kSlots * 8)[l32] = pos;
-    }
+    if (rec_wave) reinterpret_cast<int*>(stage_ptr(c) + kSlots * 8)[l32] = v.pd.x;
     return key;
   };
   // Each wave gathers only its RW rows of a chunk's K tile (all 32 when it is
@@ -518,11 +507,17 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
 template <int D, bool DENSE>
 hipError_t launch_t(const Problem& P, hipStream_t stream) {
   const dim3 grid(unsigned(P.B * P.S_q));
+  row_prep_kernel<DENSE><<<grid, 64, size_t(P.NR) * 4, stream>>>(P);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  stage_done(0, "row_prep_kernel");
   if (P.HP > 32)
-    row_export_kernel<D, DENSE, 2><<<grid, 128, ExportLds<D>::bytes(P.NR), stream>>>(P);
+    row_export_kernel<D, DENSE, 2><<<grid, 128, ExportLds<D>::kBytes, stream>>>(P);
   else
-    row_export_kernel<D, DENSE, 1><<<grid, 64, ExportLds<D>::bytes(P.NR), stream>>>(P);
-  return hipGetLastError();
+    row_export_kernel<D, DENSE, 1><<<grid, 64, ExportLds<D>::kBytes, stream>>>(P);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  stage_done(1, "row_export_kernel");
+  return hipSuccess;
 }
 
 template <int D>

@@ -11,7 +11,6 @@ namespace ibwd {
 constexpr int64_t kMaxHeads = 64;
 constexpr int kSlots = 32;          // slots per chunk in the row kernel
 constexpr int kRangeKeys = 128;     // keys per range of the two-pass dK route
-constexpr int kSinks = 32;          // sink entries after every range's records
 constexpr int kMaxRanges = 2048;    // ranges a row can be bucketed into (S_k <= 262144)
 constexpr int kMaxQueryBlock = 512;  // queries per range-kernel workgroup
 constexpr int kRecBlock = 128;       // records the range kernel stages per DMA
@@ -23,36 +22,34 @@ enum DkRoute : int {
 
 // Workspace layout of the two-pass dK route.  A row's valid slots are stored
 // as records grouped by key range (range r = key / RK), slot order within a
-// range.  Range r occupies [first_r, end_r) and is followed by 32 sink
-// entries whose key is (r+1)*RK, one past the range: a 32-slot tile that runs
-// past end_r reads sinks, which the range kernel sends to a scratch row.
-// Every range starts at a multiple of 4 entries.
+// range; range r occupies [first_r, end_r), and every range starts at a
+// multiple of 4 entries.
 //   rkd   [rows][rec_stride] int2   {key, dI bits} of the record
 //   rmask [rows][rec_stride][2] u32 sign bits [S > 0] of heads 0..31, 32..63
 //         (bit b of word g is head 32g + rotl5(b), rotl5 = 5-bit rotate left)
 //   offs  [rows][NR] int2           {first, end} record of each range
-//   rank  [rows][row_len] int32     rank of each valid slot among the row's
-//                                   slots of its range (sparse rows only)
+//   slot  [rows][row_len] int2      {record position or -1, dI bits} of every
+//                                   slot (written by the prep kernel)
 //   qt    [rows][D][HP] bf16        (w*q)^T of every row, heads padded to HP
 //   slab  [B][NQB][NR*RK][D] fp32   per query block partial dK
-// rec_stride = row_len + 36*NR (sinks and alignment) + 32 (stores of padding
-// lanes), rounded up to a multiple of 4.
+// rec_stride = row_len + 3*NR (alignment of the ranges), rounded up to a
+// multiple of 4.
 struct Layout {
   int64_t rows, row_len, rec_stride, HP, RK, NR, NQB, QBS, nchunk;
-  size_t off_rkd, off_rmask, off_offs, off_rank, off_qt, off_slab, total;
+  size_t off_rkd, off_rmask, off_offs, off_slot, off_qt, off_slab, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
-                          int64_t row_len, bool dense) {
+                          int64_t row_len) {
   Layout L{};
   L.rows = B * S_q;
   L.row_len = row_len;
   L.HP = H > 32 ? 64 : 32;
   L.RK = kRangeKeys;
   L.NR = (S_k + L.RK - 1) / L.RK;
-  L.rec_stride = (row_len + 36 * L.NR + kSlots + 3) & ~int64_t(3);  // 16-byte aligned rows
+  L.rec_stride = (row_len + 3 * L.NR + 3) & ~int64_t(3);  // 16-byte aligned rows
   // about 512 range-kernel workgroups (two per CU), at most kMaxQueryBlock
   // queries each
   int64_t nqb = (512 + L.NR * B - 1) / (L.NR * B);
@@ -72,8 +69,8 @@ inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_
   o = align256(o + recs * 8 + kRecBlock * 8);
   L.off_offs = o;
   o = align256(o + size_t(L.rows) * size_t(L.NR) * 8);
-  L.off_rank = o;
-  if (!dense) o = align256(o + size_t(L.rows) * size_t(row_len) * 4);
+  L.off_slot = o;
+  o = align256(o + size_t(L.rows) * size_t(row_len) * 8);
   L.off_qt = o;
   o = align256(o + size_t(L.rows) * size_t(D) * size_t(L.HP) * 2);
   L.off_slab = o;
@@ -103,7 +100,7 @@ struct Problem {
   int* rkd;  // int2 pairs {key, dI bits}
   uint32_t* rmask;
   int* offs;  // int2 pairs
-  int* rank;
+  int* slot;  // int2 pairs
   uint16_t* qt;
   float* slab;
   int64_t rec_stride, RK, NR, NQB, QBS, nchunk, HP;
@@ -121,8 +118,9 @@ hipError_t launch(Problem P, void* workspace, hipStream_t stream);
 // Row kernel of the atomic route (one wave per query row): dQ, dW and the fp32
 // atomic dK scatter.
 hipError_t launch_rows(const Problem& P, hipStream_t stream);
-// Row kernel of the two-pass route (one wave per query row and group of 32
-// heads): dQ, dW, the slot records and (w*q)^T.
+// Prep kernel (statistics, record layout, per-slot position and dI) and row
+// kernel of the two-pass route (one wave per query row and group of 32 heads):
+// dQ, dW, the slot records and (w*q)^T.
 hipError_t launch_rows_export(const Problem& P, hipStream_t stream);
 // Two-pass dK: range-major reduction into per query-block slabs, then the
 // fixed-order sum of the slabs into d_k.

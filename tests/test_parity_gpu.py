@@ -271,9 +271,9 @@ def test_stage_hook_reports_every_kernel(ibwd):
         b = run(ibwd, x, atomic_dk=True)
     finally:
         ibwd.set_stage_hook(None)
-    assert seen == [(0, "row_export_kernel"), (1, "dk_range_kernel"), (2, "dk_sum_kernel"),
-                    (0, "zero_u32_kernel"), (1, "row_kernel")]
+    assert seen == [(0, "row_prep_kernel"), (1, "row_export_kernel"), (2, "dk_range_kernel"),
+                    (3, "dk_sum_kernel"), (0, "zero_u32_kernel"), (1, "row_kernel")]
     c = run(ibwd, x)  # hook removed: nothing more is reported
-    assert len(seen) == 5
+    assert len(seen) == 6
     assert all(np.array_equal(u, v) for u, v in zip(a, c))
     assert_parity("hook-atomic", b, oracle.Problem.from_inputs(x).backward())
