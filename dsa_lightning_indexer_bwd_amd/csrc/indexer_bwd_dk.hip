@@ -27,8 +27,9 @@
 //   the 16-byte B-operand reads are bank-conflict free), one barrier, then
 //   every wave expands its A fragments from the table (bf16 dI where the sign
 //   bit is set, three VALU operations per pair of heads) and issues its
-//   MFMAs.  Tables and Q' tiles are double-buffered: the next query's scatter
-//   and DMA run while the current one computes.
+//   MFMAs.  Q' tiles are copied two queries ahead (three tiles), record stages
+//   three ahead (four stages) and key tables built one ahead (two tables), so
+//   the next queries' copies and scatter run while the current one computes.
 //   A key that a row selects twice (duplicate ids) keeps one record in the
 //   table; wave 0 notices the other by reading the tags back, and after the
 //   query loop the workgroup adds every such record in a pass of its own, in

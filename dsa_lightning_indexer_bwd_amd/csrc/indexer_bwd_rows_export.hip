@@ -27,12 +27,12 @@
 //
 // Per chunk of 32 slots:
 //   GEMM1  S^T[j,h]  = K_g[j,:] . Q[h,:]     v_mfma 32x32x16, M=j N=h K=d; K_g
-//          straight from the gather registers (GEMM1's A layout)
+//          read from the shared LDS tile (16-byte reads), Q in registers
 //   GEMM2  dQ'[h,d] += G'[h,j] K_g[j,d]      M=h N=d K=j; G' from GEMM1's
-//          accumulators, K_g^T read transposed from a wave-private LDS tile
+//          accumulators, K_g^T read transposed from the same tile
 // The head of lane l32 in GEMM1's N dimension is 32*g + rotl5(l32), so the
 // ballot of [S > 0] over the wave is directly the record's sign word in the
-// bit order the range kernel expands with two VALU operations per pair.
+// bit order the range kernel expands with three VALU operations per pair.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
