@@ -43,9 +43,11 @@
  *     launched, so on error the outputs are untouched.  Launch failures are
  *     reported by the HIP error of the launch; execution errors surface on the
  *     stream as usual for HIP.
- *   - dK routes.  The default route reduces the dK scatter in two passes: the
- *     row kernel exports each slot's sign mask [S > 0] and dI into the caller's
- *     workspace, and a range-major kernel computes the dK of every 128-key
+ *   - dK routes.  The default route reduces the dK scatter in two passes: a
+ *     prep kernel lays out each row's records by key range and computes every
+ *     slot's dI, the row kernel exports each slot's sign mask [S > 0] and dI
+ *     into the caller's workspace, and a range-major kernel computes the dK of
+ *     every 128-key
  *     range as a GEMM over (query, head) whose accumulators stay in the matrix
  *     cores (dI enters that GEMM rounded to bf16, like w*q), then the per
  *     query-block partial sums are added in a fixed order.  d_q, d_w and d_k
@@ -122,12 +124,13 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
 /*
  * indexer_bwd_workspace_bytes — device scratch needed by a call with these
  * arguments (dense != 0 selects indexer_bwd_dense; topk is ignored then).
- * The default route needs 16 bytes per record entry (topk + 36 per 128-key
- * range + 32 entries per row), 8 bytes per row and key range for the range
- * table, (w*q)^T in bf16 (2*H_pad*D bytes per row, H_pad = 32 or 64) and the
- * per query-block dK partial sums (about 460 MB in all at B=1, S_q=8192,
- * S_k=4096, H=64, D=128, topk=1024; about 860 MB for the dense variant at
- * that shape); IBWD_FLAG_ATOMIC_DK needs none (0).
+ * The default route needs 16 bytes per record entry (topk + 3 per 128-key
+ * range per row, for aligning the ranges), 8 bytes per slot for each slot's
+ * record position and dI, 8 bytes per row and key range for the range table,
+ * (w*q)^T in bf16 (2*H_pad*D bytes per row, H_pad = 32 or 64) and the per
+ * query-block dK partial sums (about 385 MB in all at B=1, S_q=8192, S_k=4096,
+ * H=64, D=128, topk=1024; about 990 MB for the dense variant at that shape);
+ * IBWD_FLAG_ATOMIC_DK needs none (0).
  * Returns 0 for invalid shapes as well; the call itself reports those.
  */
 size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_k, int64_t H,
