@@ -124,6 +124,9 @@ __device__ __forceinline__ void wait_vm() {
 // (it would wait for the copy before every later LDS read, the copy's own
 // destination or not) nor counts it: the kernel waits for these copies itself,
 // and the compiler's own vmcnt waits stay correct, only more conservative.
+// M0 is a reserved register, so the compiler does not save it around the
+// statement (it warns about the clobber); nothing else in this file reads M0
+// (gfx950's LDS instructions do not), and every copy sets M0 itself.
 __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* gbase, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
