@@ -235,8 +235,9 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int half = lane >> 5;
   // head group of this wave (wave-uniform: readfirstlane keeps it in a scalar)
   const int g = NG == 2 ? __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)) : 0;
-  // roles: the dI wave (softmax statistics, dI) and the record wave (range
-  // counts, ranking, records); one wave holds both when NG == 1
+  // roles: the dI wave (stages each slot's dI and key) and the record wave
+  // (stages record positions, stores the records); one wave holds both when
+  // NG == 1
   const bool dI_wave = NG == 1 || g == 1;
   const bool rec_wave = g == 0;
   const int H = int(P.H);
