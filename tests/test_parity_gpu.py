@@ -117,6 +117,17 @@ def test_ragged_and_odd_shapes(ibwd, topk, H, D, pad):
     assert_parity(f"ragged-{topk}-{H}-{D}", got, ref)
 
 
+@pytest.mark.parametrize("S_k,topk", [(40000, 700), (262144, 300)])
+def test_many_key_ranges(ibwd, S_k, topk):
+    """More than 64 key ranges of 128 keys (313, and 2048 at the largest S_k the
+    library accepts): the range scan with several ranges per lane, range ids of
+    up to 11 bits in the ballot ranking, and many range workgroups."""
+    log(f"case: many ranges S_k={S_k} topk={topk}")
+    wl = dataclasses.replace(WORKLOADS["tiny"], H=8, D=32, S_q=24, S_k=S_k, topk=topk, pad_frac=0.05)
+    x = make_inputs(wl, seed=S_k % 1000 + topk)
+    assert_parity(f"ranges-{S_k}-{topk}", run(ibwd, x), oracle.Problem.from_inputs(x).backward())
+
+
 def test_batches_local_ids_do_not_alias(ibwd):
     """B=2: positive out-of-range ids of batch 0 are padding, not keys of batch 1."""
     log("case: B=2 local ids")
