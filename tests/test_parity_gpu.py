@@ -220,6 +220,22 @@ def test_duplicate_ids(ibwd, atomic_dk):
     assert_parity(f"dup-atomic{int(atomic_dk)}", got, oracle.Problem.from_inputs(x).backward())
 
 
+@pytest.mark.parametrize("pad", [0.0, 0.4])
+def test_one_full_key_range(ibwd, pad):
+    """Every valid id of a row in the first 128-key range: that range holds all
+    the row's records (128 without padding, the range kernel's staged record
+    block exactly full) and the other ranges none."""
+    log(f"case: one full key range pad={pad}")
+    wl = dataclasses.replace(WORKLOADS["anchor"], S_q=40, S_k=512, topk=128, pad_frac=0.0)
+    x = make_inputs(wl, seed=41)
+    rng = np.random.default_rng(9)
+    for t in range(wl.S_q):
+        x.ids[0, t] = rng.permutation(128)
+    if pad:
+        x.ids[rng.random(x.ids.shape) < pad] = -1
+    assert_parity(f"full-range-{pad}", run(ibwd, x), oracle.Problem.from_inputs(x).backward())
+
+
 def test_inputs_are_not_modified(ibwd):
     log("case: inputs read-only")
     x = make_inputs("tiny")
