@@ -11,6 +11,7 @@ HIP events on the kernels' stream (through the library's stage hook); the
 roofline object describes the kernel that takes longest.
 """
 import argparse
+import dataclasses
 import json
 import os
 import statistics
@@ -32,7 +33,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=15)
     ap.add_argument("--workload", default="anchor")
+    ap.add_argument("--topk", type=int, default=0,
+                    help="override the sparse workload's topk (a topk sweep at its other shapes)")
     ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--atomic-dk", action="store_true",
+                    help="the single-pass route with fp32 atomic dK (not bitwise reproducible)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample")
@@ -56,6 +61,11 @@ def main():
 
     ibwd.library()  # fails loudly when the HIP library is missing
     wl = WORKLOADS[args.workload]
+    if args.topk:
+        if wl.dense or args.topk > wl.S_k:
+            print("--topk applies to sparse workloads, at most S_k", file=sys.stderr)
+            sys.exit(2)
+        wl = dataclasses.replace(wl, topk=args.topk)
     dev = torch.device("cuda:0")
     print("bench: generating %s inputs" % wl.name, file=sys.stderr, flush=True)
     x = make_inputs(wl, device=dev)
@@ -73,7 +83,11 @@ def main():
     dq = torch.empty((B, S_q, H, D), dtype=torch.float32, device=dev)
     dw = torch.empty((B, S_q, H), dtype=torch.float32, device=dev)
     dk = torch.empty((B, S_k, D), dtype=torch.float32, device=dev)
-    flags = ibwd.IBWD_FLAG_DETERMINISTIC if args.deterministic else 0
+    if args.deterministic and args.atomic_dk:
+        print("--deterministic and --atomic-dk exclude each other", file=sys.stderr)
+        sys.exit(2)
+    flags = (ibwd.IBWD_FLAG_DETERMINISTIC if args.deterministic else 0) | \
+        (ibwd.IBWD_FLAG_ATOMIC_DK if args.atomic_dk else 0)
     ws_bytes = ibwd.indexer_bwd_workspace_bytes(wl.dense, B, S_q, S_k, H, D, wl.topk, flags)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.Stream(device=dev)
@@ -81,10 +95,12 @@ def main():
     def step():
         if ids is None:
             ibwd.indexer_bwd_dense(q, k, w, I, p, dq, dw, dk, q_offset=wl.q_offset,
-                                   deterministic=args.deterministic, workspace=ws, stream=stream)
+                                   deterministic=args.deterministic, atomic_dk=args.atomic_dk,
+                                   workspace=ws, stream=stream)
         else:
             ibwd.indexer_bwd_sparse(q, k, w, ids, I, p, dq, dw, dk,
-                                    deterministic=args.deterministic, workspace=ws, stream=stream)
+                                    deterministic=args.deterministic, atomic_dk=args.atomic_dk,
+                                    workspace=ws, stream=stream)
 
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib << 18  # fp32 elements
@@ -154,7 +170,8 @@ def main():
                         "algorithmic_work": work, "achieved": round(ach, 3), "peak": peak,
                         "unit": unit, "frac": round(ach / peak, 4)})
     dom = max(kernels, key=lambda k: k["us_mean"])
-    traffic = measured_traffic(dom["kernel"], wl.name, bool(args.deterministic))
+    # the stored counters are for the workloads' own shapes only
+    traffic = None if args.topk else measured_traffic(dom["kernel"], wl.name, bool(args.deterministic))
 
     # algorithmic HBM bytes of one call (inputs read once, outputs written once)
     row = wl.S_k if wl.dense else wl.topk
@@ -179,7 +196,7 @@ def main():
         "config": {"workload": wl.name, "B": B, "H": H, "D": D, "S_q": S_q, "S_k": S_k,
                    "topk": None if wl.dense else wl.topk, "pad_frac": wl.pad_frac,
                    "sorted_ids": wl.sorted_ids, "dense": wl.dense,
-                   "deterministic": bool(args.deterministic)},
+                   "deterministic": bool(args.deterministic), "atomic_dk": bool(args.atomic_dk)},
         "us_per_call_median": round(med_us, 2),
         "us_per_call_mean": round(mean_us, 2),
         "us_per_call_min": round(min(per_call_ms) * 1e3, 2),

@@ -220,6 +220,19 @@ def test_duplicate_ids(ibwd, atomic_dk):
     assert_parity(f"dup-atomic{int(atomic_dk)}", got, oracle.Problem.from_inputs(x).backward())
 
 
+def test_ragged_row_lengths(ibwd):
+    """Per-row valid lengths that ramp up with the query (row t keeps its first
+    min(t//2 + 1, topk) slots, the rest are -1), at the anchor's H, D, S_k and
+    topk: every chunk count from 1 to the full row, a partial last chunk."""
+    log("case: ragged row-length ramp")
+    wl = dataclasses.replace(WORKLOADS["anchor"], S_q=2048, pad_frac=0.0)
+    x = make_inputs(wl, seed=51)
+    t = np.arange(wl.S_q)[:, None]
+    j = np.arange(wl.topk)[None, :]
+    x.ids[0][j >= np.minimum(t // 2 + 1, wl.topk)] = -1
+    assert_parity("ramp", run(ibwd, x), oracle.Problem.from_inputs(x).backward())
+
+
 @pytest.mark.parametrize("pad", [0.0, 0.4])
 def test_one_full_key_range(ibwd, pad):
     """Every valid id of a row in the first 128-key range: that range holds all
