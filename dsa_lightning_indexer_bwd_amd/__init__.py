@@ -25,6 +25,7 @@ __all__ = [
     "IBWD_ERR_HIP",
     "IBWD_FLAG_DETERMINISTIC",
     "IBWD_FLAG_ATOMIC_DK",
+    "IBWD_FLAG_GLOBAL_IDS",
     "IndexerBwdError",
 ]
 
@@ -34,6 +35,7 @@ IBWD_ERR_UNSUPPORTED_DEVICE = -2
 IBWD_ERR_HIP = -3
 IBWD_FLAG_DETERMINISTIC = 1
 IBWD_FLAG_ATOMIC_DK = 2
+IBWD_FLAG_GLOBAL_IDS = 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_indexer_bwd.so")
 _lib = None
@@ -154,12 +156,15 @@ def _flags(deterministic: bool, atomic_dk: bool) -> int:
 
 def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w=None, d_k=None, *,
                        sm_scale: float = 1.0, grad_loss: float = 1.0, deterministic: bool = False,
-                       atomic_dk: bool = False, workspace=None, stream=None) -> Tuple:
+                       atomic_dk: bool = False, global_ids: bool = False, workspace=None,
+                       stream=None) -> Tuple:
     """Backward of the top-k indexer.  Returns (d_q, d_w, d_k), all fp32.
 
     q [B,S_q,H,D] bf16, k [B,S_k,D] bf16, w [B,S_q,H] fp32, topk_ids [B,S_q,topk]
     int32, index_score / attn_score [B,S_q,topk] fp32.  Outputs are overwritten.
     atomic_dk selects the single-pass fp32-atomic dK route (no workspace).
+    global_ids: the ids index the flattened [B*S_k] keys; a row of batch b keeps
+    only ids in [b*S_k, (b+1)*S_k), every other id is padding.
     """
     torch = _torch()
     B, S_q, H, D = q.shape
@@ -175,7 +180,7 @@ def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w
     _check(d_q, torch.float32, (B, S_q, H, D), "d_q")
     _check(d_w, torch.float32, (B, S_q, H), "d_w")
     _check(d_k, torch.float32, (B, S_k, D), "d_k")
-    flags = _flags(deterministic, atomic_dk)
+    flags = _flags(deterministic, atomic_dk) | (IBWD_FLAG_GLOBAL_IDS if global_ids else 0)
     workspace, ws_bytes = _workspace(False, B, S_q, S_k, H, D, topk, flags, workspace, q.device)
     st = library().indexer_bwd_sparse(
         _ptr(q), _ptr(k), _ptr(w), _ptr(topk_ids), _ptr(index_score), _ptr(attn_score), _ptr(d_q),

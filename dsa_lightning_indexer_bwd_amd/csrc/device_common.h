@@ -102,6 +102,16 @@ __device__ __forceinline__ uint32_t write_lane(uint32_t old, uint32_t val, int l
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
+// Key of a top-k id within its batch, or -1 for a padding slot.  base is 0
+// for batch-local ids and b*S_k for ids into the flattened [B*S_k] keys of
+// batch b.  With base + S_k <= 2^31 the unsigned difference lands in
+// [0, S_k) exactly when base <= id < base + S_k: a negative id, or one below
+// base, wraps to at least 2^31 - base >= S_k.
+__device__ __forceinline__ int local_key(int id, int base, int S_k) {
+  const uint32_t local = uint32_t(id) - uint32_t(base);
+  return local < uint32_t(S_k) ? int(local) : -1;
+}
+
 // Softmax statistics of one query row over its valid slots, in base 2: with
 // c2 = sm_scale*log2(e), m2 = max_j c2*I_j and invZ = 1 / sum_j 2^(c2*I_j - m2)
 // over the slots j < n whose key_of(j, id_at(j)) >= 0.  One pass: each lane

@@ -51,7 +51,8 @@ int check_common(const void* q, const void* k, const float* w, const float* I, c
   if (D != 32 && D != 64 && D != 128) return IBWD_ERR_INVALID_ARGUMENT;
   if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, row_len))
     return IBWD_ERR_INVALID_ARGUMENT;
-  if ((flags & ~(IBWD_FLAG_DETERMINISTIC | IBWD_FLAG_ATOMIC_DK)) != 0) return IBWD_ERR_INVALID_ARGUMENT;
+  if ((flags & ~(IBWD_FLAG_DETERMINISTIC | IBWD_FLAG_ATOMIC_DK | IBWD_FLAG_GLOBAL_IDS)) != 0)
+    return IBWD_ERR_INVALID_ARGUMENT;
   if ((flags & IBWD_FLAG_DETERMINISTIC) && (flags & IBWD_FLAG_ATOMIC_DK)) return IBWD_ERR_INVALID_ARGUMENT;
   // the row kernel buckets a row's slots into at most kMaxRanges key ranges
   if ((S_k + ibwd::kRangeKeys - 1) / ibwd::kRangeKeys > ibwd::kMaxRanges)
@@ -104,6 +105,8 @@ int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32
   P.D = D;
   P.row_len = topk;
   P.dense = false;
+  // a global id of batch b is offset by b*S_k; B*S_k < 2^31 was checked above
+  P.id_batch_stride = (flags & IBWD_FLAG_GLOBAL_IDS) ? int32_t(S_k) : 0;
   P.q_offset = 0;
   P.sm_scale = sm_scale;
   P.grad_loss = grad_loss;
@@ -121,6 +124,7 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
   if (st != IBWD_OK) return st;
   if (q_offset < -(int64_t(1) << 40) || q_offset > (int64_t(1) << 40))
     return IBWD_ERR_INVALID_ARGUMENT;
+  if (flags & IBWD_FLAG_GLOBAL_IDS) return IBWD_ERR_INVALID_ARGUMENT;  // the dense call has no ids
   size_t need = workspace_bytes(B, S_q, S_k, H, D, S_k, flags);
   if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256)))
     return IBWD_ERR_INVALID_ARGUMENT;
@@ -143,6 +147,7 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
   P.D = D;
   P.row_len = S_k;
   P.dense = true;
+  P.id_batch_stride = 0;
   P.q_offset = q_offset;
   P.sm_scale = sm_scale;
   P.grad_loss = grad_loss;

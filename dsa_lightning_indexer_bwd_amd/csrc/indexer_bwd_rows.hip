@@ -85,11 +85,12 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
   const int32_t* idrow = DENSE ? nullptr : P.ids + r * P.row_len;
   const uint16_t* kb = P.k + b * P.S_k * D;
   const int S_k = int(P.S_k);
+  const int id_base = int(b) * P.id_batch_stride;
 
   auto key_of = [&](int j, int id) -> int {
     if (j >= n) return -1;
     if (DENSE) return j;
-    return (id >= 0 && id < S_k) ? id : -1;
+    return local_key(id, id_base, S_k);
   };
 
   // ---- softmax statistics over the valid slots ---------------------------------

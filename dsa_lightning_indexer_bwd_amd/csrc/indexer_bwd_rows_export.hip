@@ -129,12 +129,13 @@ __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
   int2* slot = reinterpret_cast<int2*>(P.slot) + r * P.row_len;
   int2* offrow = reinterpret_cast<int2*>(P.offs) + r * P.NR;
   const int S_k = int(P.S_k);
+  const int id_base = int(r / P.S_q) * P.id_batch_stride;
   constexpr int RK = kRangeKeys;  // power of two: divisions are shifts
   const int NR = int(P.NR);
   auto key_of = [&](int j, int id) -> int {
     if (j >= n) return -1;
     if (DENSE) return j;
-    return (id >= 0 && id < S_k) ? id : -1;
+    return local_key(id, id_base, S_k);
   };
   int nbits = 0;
   while ((1 << nbits) < NR) ++nbits;
@@ -257,11 +258,12 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int2* slotrow = reinterpret_cast<const int2*>(P.slot) + r * P.row_len;
   const uint16_t* kb = P.k + b * P.S_k * D;
   const int S_k = int(P.S_k);
+  const int id_base = int(b) * P.id_batch_stride;
 
   auto key_of = [&](int j, int id) -> int {
     if (j >= n) return -1;
     if (DENSE) return j;
-    return (id >= 0 && id < S_k) ? id : -1;
+    return local_key(id, id_base, S_k);
   };
   int2* rkd = reinterpret_cast<int2*>(P.rkd) + r * P.rec_stride;
   uint2* rmask = reinterpret_cast<uint2*>(P.rmask) + r * P.rec_stride;

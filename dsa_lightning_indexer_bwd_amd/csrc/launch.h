@@ -93,6 +93,7 @@ struct Problem {
   float* dk;            // [B,S_k,D]
   int64_t B, S_q, S_k, H, D, row_len;
   bool dense;
+  int32_t id_batch_stride;  // 0: ids are batch-local; S_k: ids index the flattened [B*S_k] keys
   int64_t q_offset;
   float sm_scale, grad_loss;
   int route;            // DkRoute

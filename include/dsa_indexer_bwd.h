@@ -80,17 +80,26 @@ extern "C" {
                                       two-pass route; conflicts with IBWD_FLAG_ATOMIC_DK) */
 #define IBWD_FLAG_ATOMIC_DK 2u     /* single-pass dK with fp32 global atomics; no workspace;
                                       d_k not bitwise reproducible */
+#define IBWD_FLAG_GLOBAL_IDS 4u    /* indexer_bwd_sparse only: topk_ids index the flattened
+                                      [B*S_k] key array instead of the batch's own keys */
 
 /*
  * indexer_bwd_sparse — backward of the top-k (sparse) indexer.
  *
- *   topk_ids     [B,S_q,topk] int32, batch-local key ids (see padding above)
+ *   topk_ids     [B,S_q,topk] int32, batch-local key ids (see padding above).
+ *                With IBWD_FLAG_GLOBAL_IDS the ids are global instead (the
+ *                factory flag topk_indices_global of PR #730's benchmark
+ *                harness): a row of batch b selects key id - b*S_k of its own
+ *                batch when b*S_k <= id < (b+1)*S_k, and every other id,
+ *                another batch's key included, is a padding slot.  At B = 1
+ *                the two conventions coincide.
  *   index_score  [B,S_q,topk] fp32, the forward scores I of the selected slots
  *   attn_score   [B,S_q,topk] fp32, the target distribution p over the valid
  *                slots (read-only; the kernel never writes it)
  *   sm_scale     scale applied to I inside the softmax and as chain factor
  *   grad_loss    upstream gradient of the KL loss (a scalar)
- *   flags        0, IBWD_FLAG_DETERMINISTIC or IBWD_FLAG_ATOMIC_DK
+ *   flags        0, IBWD_FLAG_DETERMINISTIC or IBWD_FLAG_ATOMIC_DK, optionally or-ed
+ *                with IBWD_FLAG_GLOBAL_IDS
  *   workspace    device scratch of at least indexer_bwd_workspace_bytes(...)
  *                bytes (may be NULL when that size is 0); 256-byte aligned
  *   stream       HIP stream the work is enqueued on

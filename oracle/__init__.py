@@ -78,8 +78,24 @@ def widen_bf16(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def global_ids_to_local(ids, S_k: int) -> np.ndarray:
+    """Batch-local ids of global top-k ids [B,S_q,topk].
+
+    The benchmark harness of NVIDIA/cudnn-frontend PR #730 builds its kernel
+    with topk_indices_global=True (at batch 1 only, where global and local ids
+    coincide).  Read here: a global id indexes the keys of all batches laid end
+    to end, so a row of batch b holds key id - b*S_k of its own batch when
+    b*S_k <= id < (b+1)*S_k; any other id, a key of another batch included, is
+    padding (-1), the same rule as for an out-of-range local id.
+    """
+    g = np.asarray(ids, dtype=np.int64)
+    base = (np.arange(g.shape[0], dtype=np.int64) * S_k)[:, None, None]
+    local = g - base
+    return np.where((local >= 0) & (local < S_k), local, -1).astype(np.int32)
+
+
 class Problem:
-    """Inputs of one backward call, held as fp64 (ids int32)."""
+    """Inputs of one backward call, held as fp64 (ids int32, batch-local)."""
 
     def __init__(self, q, k, w, I, p, ids=None, *, S_k=None, sm_scale=1.0, grad_loss=1.0,
                  q_offset=0):

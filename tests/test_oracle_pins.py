@@ -293,6 +293,21 @@ def test_padding_equivalence():
         assert np.array_equal(u, v)
 
 
+def test_global_ids_remap_hand_values():
+    """Global ids (topk_indices_global of the PR #730 harness) read as indices
+    into the keys of all batches laid end to end: hand-computed local ids for
+    B=2, S_k=3, with another batch's keys, -1, and the int32 extremes."""
+    row = [0, 2, 3, -1, 5, 6, 2**31 - 1, -2**31]
+    ids = np.array([[row], [row]], dtype=np.int32)
+    got = oracle.global_ids_to_local(ids, 3)
+    assert got.dtype == np.int32
+    assert got[0, 0].tolist() == [0, 2, -1, -1, -1, -1, -1, -1]
+    assert got[1, 0].tolist() == [-1, -1, 0, -1, 2, -1, -1, -1]
+    # at one batch, global and local ids coincide (out-of-range ids stay padding)
+    one = oracle.global_ids_to_local(ids[:1], 3)
+    assert one[0, 0].tolist() == [0, 2, -1, -1, -1, -1, -1, -1]
+
+
 def test_dense_equals_sparse_cross_entry():
     """dense(q,k,w,I,p) equals sparse with ids[t,j] = j if j <= t + q_offset else -1."""
     rng = np.random.default_rng(9)

@@ -158,6 +158,40 @@ def test_dense_q_offset(ibwd, q_offset):
         return
     assert_parity(f"dense-off{q_offset}", got, ref)
 
+@pytest.mark.parametrize("atomic_dk", [False, True])
+def test_global_ids(ibwd, atomic_dk):
+    """B=3 with global ids (key id - b*S_k of batch b): the valid slots of the
+    local-id case shifted by b*S_k, and its padding slots replaced by keys of
+    the other batches, ids past B*S_k and negatives.  Equal to the local-id
+    call (bitwise on the default route) and to the oracle on the remapped ids."""
+    log(f"case: B=3 global ids atomic={atomic_dk}")
+    wl = dataclasses.replace(WORKLOADS["tiny"], B=3, S_q=40, S_k=300, topk=96, pad_frac=0.3)
+    x = make_inputs(wl, seed=41)
+    S_k = wl.S_k
+    base = (np.arange(wl.B, dtype=np.int64) * S_k)[:, None, None]
+    pad = x.ids < 0
+    n = np.arange(x.ids.size).reshape(x.ids.shape)
+    other = (base + S_k * (1 + n % (wl.B - 1)) + n % S_k) % (wl.B * S_k)   # another batch's key
+    junk = np.where(n % 3 == 0, other, np.where(n % 3 == 1, wl.B * S_k + n % 7, -1 - n % 4))
+    g = np.where(pad, junk, x.ids + base).astype(np.int32)
+    local = oracle.global_ids_to_local(g, S_k)
+    assert np.array_equal(local, np.where(pad, -1, x.ids))
+    t = dev_inputs(x)
+    ref_local = run(ibwd, x, t, atomic_dk=atomic_dk)
+    tg = dict(t, ids=torch.from_numpy(g).to(t["q"].device))
+    got = ibwd.indexer_bwd_sparse(tg["q"], tg["k"], tg["w"], tg["ids"], tg["I"], tg["p"],
+                                  sm_scale=x.sm_scale, grad_loss=x.grad_loss, atomic_dk=atomic_dk,
+                                  global_ids=True)
+    torch.cuda.synchronize()
+    got = [a.cpu().numpy() for a in got]
+    assert np.array_equal(got[0], ref_local[0]) and np.array_equal(got[1], ref_local[1])
+    if atomic_dk:
+        assert relrms(got[2], ref_local[2]) < 1e-5
+    else:
+        assert np.array_equal(got[2], ref_local[2])
+    x.ids = local
+    assert_parity(f"global-atomic{int(atomic_dk)}", got, oracle.Problem.from_inputs(x).backward())
+
 
 # ---------------------------------------------------------------------------
 # padding equivalence and determinism
