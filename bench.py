@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--atomic-dk", action="store_true",
                     help="the single-pass route with fp32 atomic dK (not bitwise reproducible)")
+    ap.add_argument("--bf16-out", action="store_true",
+                    help="d_q, d_w and d_k written as bf16 (the fp32 results rounded)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample")
@@ -80,14 +82,16 @@ def main():
     ids = None if x.ids is None else torch.from_numpy(x.ids).to(dev)
     B, S_q, H, D = x.q.shape
     S_k = x.k.shape[1]
-    dq = torch.empty((B, S_q, H, D), dtype=torch.float32, device=dev)
-    dw = torch.empty((B, S_q, H), dtype=torch.float32, device=dev)
-    dk = torch.empty((B, S_k, D), dtype=torch.float32, device=dev)
-    if args.deterministic and args.atomic_dk:
-        print("--deterministic and --atomic-dk exclude each other", file=sys.stderr)
+    odt = torch.bfloat16 if args.bf16_out else torch.float32
+    dq = torch.empty((B, S_q, H, D), dtype=odt, device=dev)
+    dw = torch.empty((B, S_q, H), dtype=odt, device=dev)
+    dk = torch.empty((B, S_k, D), dtype=odt, device=dev)
+    if args.atomic_dk and (args.deterministic or args.bf16_out):
+        print("--atomic-dk excludes --deterministic and --bf16-out", file=sys.stderr)
         sys.exit(2)
     flags = (ibwd.IBWD_FLAG_DETERMINISTIC if args.deterministic else 0) | \
-        (ibwd.IBWD_FLAG_ATOMIC_DK if args.atomic_dk else 0)
+        (ibwd.IBWD_FLAG_ATOMIC_DK if args.atomic_dk else 0) | \
+        (ibwd.IBWD_FLAG_BF16_OUT if args.bf16_out else 0)
     ws_bytes = ibwd.indexer_bwd_workspace_bytes(wl.dense, B, S_q, S_k, H, D, wl.topk, flags)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.Stream(device=dev)
@@ -96,11 +100,11 @@ def main():
         if ids is None:
             ibwd.indexer_bwd_dense(q, k, w, I, p, dq, dw, dk, q_offset=wl.q_offset,
                                    deterministic=args.deterministic, atomic_dk=args.atomic_dk,
-                                   workspace=ws, stream=stream)
+                                   bf16_out=args.bf16_out, workspace=ws, stream=stream)
         else:
             ibwd.indexer_bwd_sparse(q, k, w, ids, I, p, dq, dw, dk,
                                     deterministic=args.deterministic, atomic_dk=args.atomic_dk,
-                                    workspace=ws, stream=stream)
+                                    bf16_out=args.bf16_out, workspace=ws, stream=stream)
 
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib << 18  # fp32 elements
@@ -159,7 +163,7 @@ def main():
             prev = e
     kernels = []
     for (stage, name), ts in sorted(per_kernel.items()):
-        bound, work = kernel_model(name, wl, B, H, D, S_q, S_k)
+        bound, work = kernel_model(name, wl, B, H, D, S_q, S_k, 2 if args.bf16_out else 4)
         mean_k = statistics.fmean(ts)
         if bound == "mfma":
             ach, peak, unit = work / (mean_k * 1e-6) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
@@ -171,13 +175,15 @@ def main():
                         "unit": unit, "frac": round(ach / peak, 4)})
     dom = max(kernels, key=lambda k: k["us_mean"])
     # the stored counters are for the workloads' own shapes only
-    traffic = None if args.topk else measured_traffic(dom["kernel"], wl.name, bool(args.deterministic))
+    traffic = None if (args.topk or args.bf16_out) else measured_traffic(
+        dom["kernel"], wl.name, bool(args.deterministic))
 
     # algorithmic HBM bytes of one call (inputs read once, outputs written once)
     row = wl.S_k if wl.dense else wl.topk
+    ob = 2 if args.bf16_out else 4
     hbm_bytes = (B * S_q * H * D * 2 + B * S_k * D * 2 + B * S_q * H * 4
                  + B * S_q * row * (4 + 4 + (0 if wl.dense else 4))
-                 + B * S_q * H * D * 4 + B * S_q * H * 4 + B * S_k * D * 4)
+                 + (B * S_q * H * D + B * S_q * H + B * S_k * D) * ob)
 
     out = {
         "metric": METRIC,
@@ -196,7 +202,8 @@ def main():
         "config": {"workload": wl.name, "B": B, "H": H, "D": D, "S_q": S_q, "S_k": S_k,
                    "topk": None if wl.dense else wl.topk, "pad_frac": wl.pad_frac,
                    "sorted_ids": wl.sorted_ids, "dense": wl.dense,
-                   "deterministic": bool(args.deterministic), "atomic_dk": bool(args.atomic_dk)},
+                   "deterministic": bool(args.deterministic), "atomic_dk": bool(args.atomic_dk),
+                   "bf16_out": bool(args.bf16_out)},
         "us_per_call_median": round(med_us, 2),
         "us_per_call_mean": round(mean_us, 2),
         "us_per_call_min": round(min(per_call_ms) * 1e3, 2),
@@ -224,14 +231,15 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def kernel_model(name, wl, B, H, D, S_q, S_k):
+def kernel_model(name, wl, B, H, D, S_q, S_k, out_bytes=4):
     """(bound, algorithmic work per launch) of one kernel of the call.
 
     Work units per query row are the row's slots (topk, or t+1 for the dense
     variant): the prep kernel reads the slot inputs and writes one 8-byte
     {position, dI} per slot, the row kernels do GEMM1 + GEMM2 (4*H*D FLOP per slot), the range
     kernel the dK GEMM (2*H*D per slot), the atomic-route row kernel all three.
-    The slab sum reads every query block's partial dK once and writes d_k."""
+    The slab sum reads every query block's partial dK once and writes d_k
+    (out_bytes per element)."""
     slots = wl.flops() // (6 * H * D)
     if name == "row_prep_kernel":
         # ids (sparse), I and p read once, {position, dI} written per slot
@@ -250,7 +258,7 @@ def kernel_model(name, wl, B, H, D, S_q, S_k):
         nqb = max(1, min(nqb, S_q))
         qbs = -(-S_q // nqb)
         nqb = -(-S_q // qbs)
-        return "hbm", (nqb + 1) * B * S_k * D * 4
+        return "hbm", (nqb * 4 + out_bytes) * B * S_k * D
     if name == "zero_u32_kernel":
         return "hbm", B * S_k * D * 4
     raise KeyError(name)

@@ -26,6 +26,7 @@ __all__ = [
     "IBWD_FLAG_DETERMINISTIC",
     "IBWD_FLAG_ATOMIC_DK",
     "IBWD_FLAG_GLOBAL_IDS",
+    "IBWD_FLAG_BF16_OUT",
     "IndexerBwdError",
 ]
 
@@ -36,6 +37,7 @@ IBWD_ERR_HIP = -3
 IBWD_FLAG_DETERMINISTIC = 1
 IBWD_FLAG_ATOMIC_DK = 2
 IBWD_FLAG_GLOBAL_IDS = 4
+IBWD_FLAG_BF16_OUT = 8
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_indexer_bwd.so")
 _lib = None
@@ -123,17 +125,18 @@ def _stream_handle(stream, device) -> int:
     return int(s.cuda_stream)
 
 
-def _outputs(q, k, d_q, d_w, d_k):
+def _outputs(q, k, d_q, d_w, d_k, bf16_out):
+    """The three outputs (allocated when None), checked for dtype and shape."""
     torch = _torch()
     B, S_q, H, D = q.shape
     S_k = k.shape[1]
-    if d_q is None:
-        d_q = torch.empty((B, S_q, H, D), dtype=torch.float32, device=q.device)
-    if d_w is None:
-        d_w = torch.empty((B, S_q, H), dtype=torch.float32, device=q.device)
-    if d_k is None:
-        d_k = torch.empty((B, S_k, D), dtype=torch.float32, device=q.device)
-    return d_q, d_w, d_k
+    dt = torch.bfloat16 if bf16_out else torch.float32
+    shapes = ((B, S_q, H, D), (B, S_q, H), (B, S_k, D))
+    out = [torch.empty(s, dtype=dt, device=q.device) if t is None else t
+           for t, s in zip((d_q, d_w, d_k), shapes)]
+    for t, s, name in zip(out, shapes, ("d_q", "d_w", "d_k")):
+        _check(t, dt, s, name)
+    return tuple(out)
 
 
 def _workspace(dense, B, S_q, S_k, H, D, topk, flags, workspace, device):
@@ -150,15 +153,17 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
-def _flags(deterministic: bool, atomic_dk: bool) -> int:
-    return (IBWD_FLAG_DETERMINISTIC if deterministic else 0) | (IBWD_FLAG_ATOMIC_DK if atomic_dk else 0)
+def _flags(deterministic: bool, atomic_dk: bool, bf16_out: bool) -> int:
+    return ((IBWD_FLAG_DETERMINISTIC if deterministic else 0) | (IBWD_FLAG_ATOMIC_DK if atomic_dk else 0)
+            | (IBWD_FLAG_BF16_OUT if bf16_out else 0))
 
 
 def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w=None, d_k=None, *,
                        sm_scale: float = 1.0, grad_loss: float = 1.0, deterministic: bool = False,
-                       atomic_dk: bool = False, global_ids: bool = False, workspace=None,
-                       stream=None) -> Tuple:
-    """Backward of the top-k indexer.  Returns (d_q, d_w, d_k), all fp32.
+                       atomic_dk: bool = False, global_ids: bool = False, bf16_out: bool = False,
+                       workspace=None, stream=None) -> Tuple:
+    """Backward of the top-k indexer.  Returns (d_q, d_w, d_k), all fp32, or all
+    bf16 with bf16_out (the fp32 results rounded to nearest even; not with atomic_dk).
 
     q [B,S_q,H,D] bf16, k [B,S_k,D] bf16, w [B,S_q,H] fp32, topk_ids [B,S_q,topk]
     int32, index_score / attn_score [B,S_q,topk] fp32.  Outputs are overwritten.
@@ -176,11 +181,8 @@ def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w
     _check(topk_ids, torch.int32, (B, S_q, topk), "topk_ids")
     _check(index_score, torch.float32, (B, S_q, topk), "index_score")
     _check(attn_score, torch.float32, (B, S_q, topk), "attn_score")
-    d_q, d_w, d_k = _outputs(q, k, d_q, d_w, d_k)
-    _check(d_q, torch.float32, (B, S_q, H, D), "d_q")
-    _check(d_w, torch.float32, (B, S_q, H), "d_w")
-    _check(d_k, torch.float32, (B, S_k, D), "d_k")
-    flags = _flags(deterministic, atomic_dk) | (IBWD_FLAG_GLOBAL_IDS if global_ids else 0)
+    d_q, d_w, d_k = _outputs(q, k, d_q, d_w, d_k, bf16_out)
+    flags = _flags(deterministic, atomic_dk, bf16_out) | (IBWD_FLAG_GLOBAL_IDS if global_ids else 0)
     workspace, ws_bytes = _workspace(False, B, S_q, S_k, H, D, topk, flags, workspace, q.device)
     st = library().indexer_bwd_sparse(
         _ptr(q), _ptr(k), _ptr(w), _ptr(topk_ids), _ptr(index_score), _ptr(attn_score), _ptr(d_q),
@@ -193,11 +195,12 @@ def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w
 
 def indexer_bwd_dense(q, k, w, index_score, attn_score, d_q=None, d_w=None, d_k=None, *,
                       q_offset: int = 0, sm_scale: float = 1.0, grad_loss: float = 1.0,
-                      deterministic: bool = False, atomic_dk: bool = False, workspace=None,
-                      stream=None) -> Tuple:
+                      deterministic: bool = False, atomic_dk: bool = False,
+                      bf16_out: bool = False, workspace=None, stream=None) -> Tuple:
     """Backward of the dense causal indexer (key s selected iff s <= t + q_offset).
 
-    index_score / attn_score are [B,S_q,S_k] fp32.  Returns (d_q, d_w, d_k).
+    index_score / attn_score are [B,S_q,S_k] fp32.  Returns (d_q, d_w, d_k), fp32 or
+    (bf16_out) bf16.
     """
     torch = _torch()
     B, S_q, H, D = q.shape
@@ -207,11 +210,8 @@ def indexer_bwd_dense(q, k, w, index_score, attn_score, d_q=None, d_w=None, d_k=
     _check(w, torch.float32, (B, S_q, H), "w")
     _check(index_score, torch.float32, (B, S_q, S_k), "index_score")
     _check(attn_score, torch.float32, (B, S_q, S_k), "attn_score")
-    d_q, d_w, d_k = _outputs(q, k, d_q, d_w, d_k)
-    _check(d_q, torch.float32, (B, S_q, H, D), "d_q")
-    _check(d_w, torch.float32, (B, S_q, H), "d_w")
-    _check(d_k, torch.float32, (B, S_k, D), "d_k")
-    flags = _flags(deterministic, atomic_dk)
+    d_q, d_w, d_k = _outputs(q, k, d_q, d_w, d_k, bf16_out)
+    flags = _flags(deterministic, atomic_dk, bf16_out)
     workspace, ws_bytes = _workspace(True, B, S_q, S_k, H, D, S_k, flags, workspace, q.device)
     st = library().indexer_bwd_dense(
         _ptr(q), _ptr(k), _ptr(w), _ptr(index_score), _ptr(attn_score), _ptr(d_q), _ptr(d_w),

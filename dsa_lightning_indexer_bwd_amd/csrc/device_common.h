@@ -40,6 +40,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   v[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, v);
 }
+// One float -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t bf16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 

@@ -43,7 +43,7 @@ bool fits(int64_t a, int64_t b, int64_t c, int64_t d) { return fits(a, b, c) && 
 
 // Shape and pointer checks common to both entry points.
 int check_common(const void* q, const void* k, const float* w, const float* I, const float* p,
-                 float* d_q, float* d_w, float* d_k, int64_t B, int64_t S_q, int64_t S_k,
+                 void* d_q, void* d_w, void* d_k, int64_t B, int64_t S_q, int64_t S_k,
                  int64_t H, int64_t D, int64_t row_len, uint32_t flags) {
   if (!q || !k || !w || !I || !p || !d_q || !d_w || !d_k) return IBWD_ERR_INVALID_ARGUMENT;
   if (B < 1 || S_q < 1 || S_k < 1 || H < 1 || D < 1 || row_len < 1) return IBWD_ERR_INVALID_ARGUMENT;
@@ -51,9 +51,12 @@ int check_common(const void* q, const void* k, const float* w, const float* I, c
   if (D != 32 && D != 64 && D != 128) return IBWD_ERR_INVALID_ARGUMENT;
   if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, row_len))
     return IBWD_ERR_INVALID_ARGUMENT;
-  if ((flags & ~(IBWD_FLAG_DETERMINISTIC | IBWD_FLAG_ATOMIC_DK | IBWD_FLAG_GLOBAL_IDS)) != 0)
+  if ((flags & ~(IBWD_FLAG_DETERMINISTIC | IBWD_FLAG_ATOMIC_DK | IBWD_FLAG_GLOBAL_IDS |
+                 IBWD_FLAG_BF16_OUT)) != 0)
     return IBWD_ERR_INVALID_ARGUMENT;
   if ((flags & IBWD_FLAG_DETERMINISTIC) && (flags & IBWD_FLAG_ATOMIC_DK)) return IBWD_ERR_INVALID_ARGUMENT;
+  // the atomic route accumulates dK in d_k itself, which needs fp32
+  if ((flags & IBWD_FLAG_BF16_OUT) && (flags & IBWD_FLAG_ATOMIC_DK)) return IBWD_ERR_INVALID_ARGUMENT;
   // the row kernel buckets a row's slots into at most kMaxRanges key ranges
   if ((S_k + ibwd::kRangeKeys - 1) / ibwd::kRangeKeys > ibwd::kMaxRanges)
     return IBWD_ERR_INVALID_ARGUMENT;
@@ -75,8 +78,8 @@ size_t workspace_bytes(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D
 extern "C" {
 
 int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32_t* topk_ids,
-                       const float* index_score, const float* attn_score, float* d_q, float* d_w,
-                       float* d_k, int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
+                       const float* index_score, const float* attn_score, void* d_q, void* d_w,
+                       void* d_k, int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
                        int64_t topk, float sm_scale, float grad_loss, uint32_t flags,
                        void* workspace, size_t ws_bytes, hipStream_t stream) {
   int st = check_common(q, k, w, index_score, attn_score, d_q, d_w, d_k, B, S_q, S_k, H, D, topk,
@@ -95,9 +98,10 @@ int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32
   P.ids = topk_ids;
   P.I = index_score;
   P.p = attn_score;
-  P.dq = d_q;
-  P.dw = d_w;
-  P.dk = d_k;
+  P.dq = static_cast<float*>(d_q);
+  P.dw = static_cast<float*>(d_w);
+  P.dk = static_cast<float*>(d_k);
+  P.bf16_out = (flags & IBWD_FLAG_BF16_OUT) != 0;
   P.B = B;
   P.S_q = S_q;
   P.S_k = S_k;
@@ -115,7 +119,7 @@ int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32
 }
 
 int indexer_bwd_dense(const void* q, const void* k, const float* w, const float* index_score,
-                      const float* attn_score, float* d_q, float* d_w, float* d_k, int64_t B,
+                      const float* attn_score, void* d_q, void* d_w, void* d_k, int64_t B,
                       int64_t S_q, int64_t S_k, int64_t H, int64_t D, int64_t q_offset,
                       float sm_scale, float grad_loss, uint32_t flags, void* workspace,
                       size_t ws_bytes, hipStream_t stream) {
@@ -137,9 +141,10 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
   P.ids = nullptr;
   P.I = index_score;
   P.p = attn_score;
-  P.dq = d_q;
-  P.dw = d_w;
-  P.dk = d_k;
+  P.dq = static_cast<float*>(d_q);
+  P.dw = static_cast<float*>(d_w);
+  P.dk = static_cast<float*>(d_k);
+  P.bf16_out = (flags & IBWD_FLAG_BF16_OUT) != 0;
   P.B = B;
   P.S_q = S_q;
   P.S_k = S_k;

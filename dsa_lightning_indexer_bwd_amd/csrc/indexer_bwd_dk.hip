@@ -514,7 +514,8 @@ dk_range_kernel(Problem P) {
     }
 }
 
-// d_k[b][s][:] = sum over query blocks (in order) of the slabs.
+// d_k[b][s][:] = sum over query blocks (in order) of the slabs; stored as fp32,
+// or rounded to bf16 (nearest even) for bf16 outputs.
 __global__ __launch_bounds__(256) void dk_sum_kernel(Problem P) {
   const int64_t D4 = P.D / 4;
   const int64_t n = P.B * P.S_k * D4;
@@ -532,7 +533,10 @@ __global__ __launch_bounds__(256) void dk_sum_kernel(Problem P) {
       a.z += v.z;
       a.w += v.w;
     }
-    reinterpret_cast<float4*>(P.dk)[i] = a;
+    if (P.bf16_out)
+      reinterpret_cast<uint2*>(P.dk)[i] = make_uint2(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w));
+    else
+      reinterpret_cast<float4*>(P.dk)[i] = a;
   }
 }
 

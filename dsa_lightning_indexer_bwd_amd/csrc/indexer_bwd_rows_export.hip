@@ -488,23 +488,31 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // ---- row epilogue: dQ = w * dQ', dW -----------------------------------------
   // dQ' register 4*i + rr of lane (half) is GEMM2's row m = 8*i + 4*half + rr,
-  // i.e. head 32*g + rotl5(m)
-  float* dqrow = P.dq + r * P.H * D;
+  // i.e. head 32*g + rotl5(m).  bf16 outputs round the same fp32 values.
+  const float tot = dw_acc + __shfl_xor(dw_acc, 32, 64);
+  auto epilogue = [&](auto* dq, auto* dw, auto cvt) {
+    auto* dqrow = dq + r * P.H * D;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int mrow = 8 * i + 4 * half + rr;
-      const int h = 32 * g + rotl5(mrow);
-      const float wh = __shfl(wv, mrow, 64);  // lane mrow holds w of that head
-      if (h < H) {
+      for (int rr = 0; rr < 4; ++rr) {
+        const int mrow = 8 * i + 4 * half + rr;
+        const int h = 32 * g + rotl5(mrow);
+        const float wh = __shfl(wv, mrow, 64);  // lane mrow holds w of that head
+        if (h < H) {
 #pragma unroll
-        for (int nd = 0; nd < ND; ++nd) dqrow[h * D + l32 + 32 * nd] = wh * dqacc[nd][4 * i + rr];
+          for (int nd = 0; nd < ND; ++nd)
+            dqrow[h * D + l32 + 32 * nd] = cvt(wh * dqacc[nd][4 * i + rr]);
+        }
       }
     }
-  }
-  const float tot = dw_acc + __shfl_xor(dw_acc, 32, 64);
-  if (half == 0 && hl < H) P.dw[r * P.H + hl] = tot;
+    if (half == 0 && hl < H) dw[r * P.H + hl] = cvt(tot);
+  };
+  if (P.bf16_out)
+    epilogue(reinterpret_cast<uint16_t*>(P.dq), reinterpret_cast<uint16_t*>(P.dw),
+             [](float v) { return bf16_bits(v); });
+  else
+    epilogue(P.dq, P.dw, [](float v) { return v; });
 }
 
 template <int D, bool DENSE>

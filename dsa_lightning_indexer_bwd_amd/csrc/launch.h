@@ -88,11 +88,12 @@ struct Problem {
   const int32_t* ids;   // [B,S_q,row_len] (sparse) or nullptr (dense)
   const float* I;       // [B,S_q,row_len]
   const float* p;       // [B,S_q,row_len]
-  float* dq;            // [B,S_q,H,D]
-  float* dw;            // [B,S_q,H]
-  float* dk;            // [B,S_k,D]
+  float* dq;            // [B,S_q,H,D]  (bf16 bits when bf16_out)
+  float* dw;            // [B,S_q,H]    (bf16 bits when bf16_out)
+  float* dk;            // [B,S_k,D]    (bf16 bits when bf16_out)
   int64_t B, S_q, S_k, H, D, row_len;
   bool dense;
+  bool bf16_out;            // outputs rounded to bf16 (nearest even) instead of fp32
   int32_t id_batch_stride;  // 0: ids are batch-local; S_k: ids index the flattened [B*S_k] keys
   int64_t q_offset;
   float sm_scale, grad_loss;

@@ -22,7 +22,8 @@
  *     of the current HIP device.  bf16 tensors are passed as their 16-bit
  *     patterns (`const void*`).
  *   - Shapes: q [B,S_q,H,D] bf16, k [B,S_k,D] bf16, w [B,S_q,H] fp32,
- *     d_q [B,S_q,H,D] fp32, d_w [B,S_q,H] fp32, d_k [B,S_k,D] fp32.
+ *     d_q [B,S_q,H,D], d_w [B,S_q,H], d_k [B,S_k,D], all fp32, or all bf16
+ *     with IBWD_FLAG_BF16_OUT.
  *   - Ids are local to each batch: 0 <= id < S_k selects key id of the same
  *     batch; every other value (-1 canonically, any negative, any >= S_k) is a
  *     padding slot that contributes nothing, whatever index_score/attn_score
@@ -82,6 +83,11 @@ extern "C" {
                                       d_k not bitwise reproducible */
 #define IBWD_FLAG_GLOBAL_IDS 4u    /* indexer_bwd_sparse only: topk_ids index the flattened
                                       [B*S_k] key array instead of the batch's own keys */
+#define IBWD_FLAG_BF16_OUT 8u      /* d_q, d_w and d_k are bf16 arrays: each element is the
+                                      fp32 result of the same call without this flag, rounded
+                                      to nearest even (PR #730 harness: bf16 dQ and dW, dK cast
+                                      to bf16).  Default route only; not with
+                                      IBWD_FLAG_ATOMIC_DK, whose dK accumulates in d_k */
 
 /*
  * indexer_bwd_sparse — backward of the top-k (sparse) indexer.
@@ -99,7 +105,9 @@ extern "C" {
  *   sm_scale     scale applied to I inside the softmax and as chain factor
  *   grad_loss    upstream gradient of the KL loss (a scalar)
  *   flags        0, IBWD_FLAG_DETERMINISTIC or IBWD_FLAG_ATOMIC_DK, optionally or-ed
- *                with IBWD_FLAG_GLOBAL_IDS
+ *                with IBWD_FLAG_GLOBAL_IDS and (not with IBWD_FLAG_ATOMIC_DK)
+ *                IBWD_FLAG_BF16_OUT
+ *   d_q, d_w, d_k  outputs: fp32, or bf16 bit patterns with IBWD_FLAG_BF16_OUT
  *   workspace    device scratch of at least indexer_bwd_workspace_bytes(...)
  *                bytes (may be NULL when that size is 0); 256-byte aligned
  *   stream       HIP stream the work is enqueued on
@@ -107,8 +115,8 @@ extern "C" {
  * Returns IBWD_OK or one of the IBWD_ERR_* codes.
  */
 int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32_t* topk_ids,
-                       const float* index_score, const float* attn_score, float* d_q, float* d_w,
-                       float* d_k, int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
+                       const float* index_score, const float* attn_score, void* d_q, void* d_w,
+                       void* d_k, int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
                        int64_t topk, float sm_scale, float grad_loss, uint32_t flags,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -125,7 +133,7 @@ int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32
  * Other arguments as for indexer_bwd_sparse.
  */
 int indexer_bwd_dense(const void* q, const void* k, const float* w, const float* index_score,
-                      const float* attn_score, float* d_q, float* d_w, float* d_k, int64_t B,
+                      const float* attn_score, void* d_q, void* d_w, void* d_k, int64_t B,
                       int64_t S_q, int64_t S_k, int64_t H, int64_t D, int64_t q_offset,
                       float sm_scale, float grad_loss, uint32_t flags, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);

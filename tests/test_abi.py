@@ -66,7 +66,7 @@ def call_sparse(a):
     dict(q=None), dict(k=None), dict(w=None), dict(ids=None), dict(I=None), dict(p=None),
     dict(dq=None), dict(dw=None), dict(dk=None),
     dict(B=0), dict(S_q=0), dict(S_k=-1), dict(H=0), dict(H=65), dict(D=48), dict(D=256),
-    dict(topk=0), dict(flags=3), dict(flags=7), dict(flags=8), dict(flags=12), dict(q=A + 8), dict(dk=A + 0x800004),
+    dict(topk=0), dict(flags=3), dict(flags=7), dict(flags=10), dict(flags=16), dict(q=A + 8), dict(dk=A + 0x800004),
     dict(w=A + 0x200002), dict(ws=None, ws_bytes=0), dict(ws=A + 0x900000, ws_bytes=16),
     dict(ws=A + 0x900010, ws_bytes=1 << 30), dict(flags=1, ws=None, ws_bytes=1 << 30),
     dict(B=1 << 20, S_q=1 << 20, H=64, D=128), dict(S_k=1024 * 256 + 1, D=128, ws_bytes=1 << 40),
@@ -89,7 +89,8 @@ def test_dense_rejects_invalid_arguments():
     assert lib.indexer_bwd_dense(*base, 1, 16, 0, 4, 32, 0, 1.0, 1.0, 0, None, 0,
                                  None) == ibwd.IBWD_ERR_INVALID_ARGUMENT
     # the dense call has no ids, so the global-id flag is an error there
-    for flags in (ibwd.IBWD_FLAG_GLOBAL_IDS, ibwd.IBWD_FLAG_GLOBAL_IDS | ibwd.IBWD_FLAG_ATOMIC_DK):
+    for flags in (ibwd.IBWD_FLAG_GLOBAL_IDS, ibwd.IBWD_FLAG_GLOBAL_IDS | ibwd.IBWD_FLAG_ATOMIC_DK,
+                  ibwd.IBWD_FLAG_BF16_OUT | ibwd.IBWD_FLAG_ATOMIC_DK):
         assert lib.indexer_bwd_dense(*base, 1, 16, 16, 4, 32, 0, 1.0, 1.0, flags, A + 0x1000000,
                                      1 << 30, None) == ibwd.IBWD_ERR_INVALID_ARGUMENT
 
@@ -103,7 +104,9 @@ def test_valid_arguments_without_gpu_fail_cleanly():
     G = ibwd.IBWD_FLAG_GLOBAL_IDS
     for a in (sparse_args(), sparse_args(flags=ibwd.IBWD_FLAG_ATOMIC_DK, ws=None, ws_bytes=0),
               sparse_args(flags=G), sparse_args(flags=G | ibwd.IBWD_FLAG_DETERMINISTIC),
-              sparse_args(flags=G | ibwd.IBWD_FLAG_ATOMIC_DK, ws=None, ws_bytes=0)):
+              sparse_args(flags=G | ibwd.IBWD_FLAG_ATOMIC_DK, ws=None, ws_bytes=0),
+              sparse_args(flags=ibwd.IBWD_FLAG_BF16_OUT),
+              sparse_args(flags=G | ibwd.IBWD_FLAG_BF16_OUT | ibwd.IBWD_FLAG_DETERMINISTIC)):
         assert call_sparse(a) in (ibwd.IBWD_ERR_HIP, ibwd.IBWD_ERR_UNSUPPORTED_DEVICE)
 
 

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from synth import WORKLOADS, make_inputs
-from tests.util import maxabs, relrms
+from tests.util import bf16_bits_to_f32, bf16_rne_bits, maxabs, relrms
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -22,6 +22,10 @@ pytestmark = pytest.mark.gpu
 DQ_DW_REL = 2e-3
 DQ_DW_MAXABS = 1e-2
 DK_REL = 5e-3
+# bf16 outputs: rounding to nearest changes each value by at most its unit
+# roundoff 2^-8 (8 significant bits), so ||bf16 - ref|| <= ||fp32 - ref|| +
+# 2^-8 ||fp32||: each bar grows by 2^-8 (times 1 + bar for ||fp32|| / ||ref||)
+BF16_U = 2.0 ** -8
 
 
 @pytest.fixture(scope="module")
@@ -49,21 +53,32 @@ def dev_inputs(x):
     return out
 
 
-def run(ibwd, x, t=None, deterministic=False, atomic_dk=False):
-    t = dev_inputs(x) if t is None else t
+def call(ibwd, x, t, outs=(None, None, None), **kw):
+    """Enqueue one library call on the current stream (no synchronisation)."""
     if x.ids is None:
-        r = ibwd.indexer_bwd_dense(t["q"], t["k"], t["w"], t["I"], t["p"], q_offset=x.wl.q_offset,
-                                   sm_scale=x.sm_scale, grad_loss=x.grad_loss,
-                                   deterministic=deterministic, atomic_dk=atomic_dk)
-    else:
-        r = ibwd.indexer_bwd_sparse(t["q"], t["k"], t["w"], t["ids"], t["I"], t["p"],
-                                    sm_scale=x.sm_scale, grad_loss=x.grad_loss,
-                                    deterministic=deterministic, atomic_dk=atomic_dk)
+        return ibwd.indexer_bwd_dense(t["q"], t["k"], t["w"], t["I"], t["p"], *outs,
+                                      q_offset=x.wl.q_offset, sm_scale=x.sm_scale,
+                                      grad_loss=x.grad_loss, **kw)
+    return ibwd.indexer_bwd_sparse(t["q"], t["k"], t["w"], t["ids"], t["I"], t["p"], *outs,
+                                   sm_scale=x.sm_scale, grad_loss=x.grad_loss, **kw)
+
+
+def host(r):
+    """Outputs as numpy: fp32 values, bf16 as their uint16 bit patterns."""
+    return [a.view(torch.int16).cpu().numpy().view(np.uint16) if a.dtype == torch.bfloat16
+            else a.cpu().numpy() for a in r]
+
+
+def run(ibwd, x, t=None, deterministic=False, atomic_dk=False, bf16_out=False):
+    t = dev_inputs(x) if t is None else t
+    r = call(ibwd, x, t, deterministic=deterministic, atomic_dk=atomic_dk, bf16_out=bf16_out)
     torch.cuda.synchronize()
-    return [a.cpu().numpy() for a in r]
+    return host(r)
 
 
-def assert_parity(name, got, ref):
+def assert_parity(name, got, ref, round_u=0.0):
+    """The bars above; round_u > 0 widens each by an output rounding of that
+    unit roundoff (bf16 outputs)."""
     dq, dw, dk = got
     rq, rw, rk = ref
     e = dict(dq=relrms(dq, rq), dw=relrms(dw, rw), dk=relrms(dk, rk),
@@ -72,9 +87,12 @@ def assert_parity(name, got, ref):
     log(f"{name}: " + " ".join(f"{k}={v:.3e}" for k, v in e.items()))
     for a in (dq, dw, dk):
         assert np.isfinite(a).all()
-    assert e["dq"] <= DQ_DW_REL and e["dq_max"] <= DQ_DW_MAXABS, e
-    assert e["dw"] <= DQ_DW_REL and e["dw_max"] <= DQ_DW_MAXABS, e
-    assert e["dk"] <= DK_REL, e
+
+    def bar(b):
+        return b + round_u * (1.0 + b)
+    assert e["dq"] <= bar(DQ_DW_REL) and e["dq_max"] <= bar(DQ_DW_MAXABS), e
+    assert e["dw"] <= bar(DQ_DW_REL) and e["dw_max"] <= bar(DQ_DW_MAXABS), e
+    assert e["dk"] <= bar(DK_REL), e
     return e
 
 
@@ -191,6 +209,62 @@ def test_global_ids(ibwd, atomic_dk):
         assert np.array_equal(got[2], ref_local[2])
     x.ids = local
     assert_parity(f"global-atomic{int(atomic_dk)}", got, oracle.Problem.from_inputs(x).backward())
+
+
+@pytest.mark.parametrize("name,S_q", [("tiny", 64), ("anchor", 192), ("dense", 160)])
+def test_bf16_outputs(ibwd, name, S_q):
+    """bf16 outputs are the fp32 outputs of the same call rounded to nearest
+    even, bit for bit, and within the widened bars of the oracle."""
+    log(f"case: bf16 outputs {name} S_q={S_q}")
+    x = make_inputs(name, S_q=S_q, seed=51)
+    t = dev_inputs(x)
+    f32 = run(ibwd, x, t)
+    b16 = run(ibwd, x, t, bf16_out=True)
+    for a, b in zip(f32, b16):
+        assert b.dtype == np.uint16
+        assert np.array_equal(b, bf16_rne_bits(a))
+    assert_parity(f"bf16-{name}", [bf16_bits_to_f32(b) for b in b16],
+                  oracle.Problem.from_inputs(x).backward(), round_u=BF16_U)
+
+
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_graph_capture_replays(ibwd, bf16_out):
+    """The call captured in a HIP graph (the library enqueues kernels only, no
+    allocation, memset or host synchronisation): every replay, with eager
+    library calls on other inputs and synchronisations in between, is bitwise
+    equal to the eager call."""
+    log(f"case: graph capture bf16_out={bf16_out}")
+    x = make_inputs("anchor", S_q=256, seed=61)
+    y = make_inputs("anchor", S_q=256, seed=62)
+    tx, ty = dev_inputs(x), dev_inputs(y)
+    ref = run(ibwd, x, tx, bf16_out=bf16_out)
+    dt = torch.bfloat16 if bf16_out else torch.float32
+    B, S_q, H, D = tx["q"].shape
+    S_k = tx["k"].shape[1]
+    outs = (torch.empty((B, S_q, H, D), dtype=dt, device="cuda:0"),
+            torch.empty((B, S_q, H), dtype=dt, device="cuda:0"),
+            torch.empty((B, S_k, D), dtype=dt, device="cuda:0"))
+    ws_bytes = ibwd.indexer_bwd_workspace_bytes(False, B, S_q, S_k, H, D, tx["ids"].shape[-1], 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):          # warm-up on the capture stream
+        call(ibwd, x, tx, outs, bf16_out=bf16_out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(ibwd, x, tx, outs, bf16_out=bf16_out, workspace=ws)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        other = run(ibwd, y, ty, bf16_out=bf16_out)   # eager work on other inputs
+        assert not np.array_equal(other[0], ref[0])
+        g.replay()
+        torch.cuda.synchronize()
+        for u, v in zip(host(outs), ref):
+            assert np.array_equal(u, v), rep
+    del g
 
 
 # ---------------------------------------------------------------------------
