@@ -1,4 +1,5 @@
-"""fp64 CPU oracle of the lightning-indexer backward (test infrastructure).
+"""fp64 CPU oracle of the lightning-indexer backward, and of the forward scores
+and top-k selection that feed it (test infrastructure).
 
 Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -203,3 +204,53 @@ class Problem:
             raise RuntimeError("oracle failed: %d" % rc)
         return dI
 
+
+
+# ---------------------------------------------------------------------------
+# the step before the backward: indexer forward scores and top-k selection
+
+def forward_scores(q, k, w, q_offset: Optional[int] = None) -> np.ndarray:
+    """Indexer scores I [B,S_q,S_k] in fp64: I[t,s] = sum_h w[t,h]*relu(q[t,h,:].k[s,:]).
+
+    This is the score whose gradients the fp64 `ref_grads` reference of the
+    NVIDIA/cudnn-frontend PR #730 benchmark harness computes (its dW is the
+    sum of g*relu(S), so dI/dw = relu(S)).  q_offset None: every key of the
+    batch; otherwise key s is visible to query t iff s <= t + q_offset (the
+    dense causal variant's rule) and masked keys score -inf.
+    """
+    q, k, w = _d(q), _d(k), _d(w)
+    B, S_q, H, D = q.shape
+    S_k = k.shape[1]
+    out = np.empty((B, S_q, S_k))
+    for b in range(B):
+        S = np.matmul(q[b], k[b].T)                          # [S_q,H,S_k]
+        out[b] = np.einsum("th,ths->ts", w[b], np.maximum(S, 0.0))
+    if q_offset is not None:
+        t = np.arange(S_q)[:, None]
+        s = np.arange(S_k)[None, :]
+        out[:, s > t + q_offset] = -np.inf
+    return out
+
+
+def select_topk(scores, topk: int):
+    """Top-k selection of each row of scores [..., S_k]: (ids int32, values).
+
+    Keys with a finite score are candidates; the row keeps its min(topk,
+    candidates) largest, a tie going to the lower key id, listed in
+    ascending key id; the remaining slots hold id -1 and value -inf.
+    """
+    sc = np.asarray(scores)
+    lead = sc.shape[:-1]
+    S_k = sc.shape[-1]
+    flat = sc.reshape(-1, S_k)
+    ids = np.full((flat.shape[0], topk), -1, dtype=np.int32)
+    vals = np.full((flat.shape[0], topk), -np.inf, dtype=sc.dtype)
+    key = np.arange(S_k)
+    for r in range(flat.shape[0]):
+        row = flat[r]
+        cand = np.flatnonzero(np.isfinite(row))
+        order = cand[np.lexsort((key[cand], -row[cand]))][:topk]   # score desc, then id asc
+        keep = np.sort(order)
+        ids[r, :keep.size] = keep
+        vals[r, :keep.size] = row[keep]
+    return ids.reshape(lead + (topk,)), vals.reshape(lead + (topk,))
