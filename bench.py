@@ -40,6 +40,9 @@ def parse():
                     help="the single-pass route with fp32 atomic dK (not bitwise reproducible)")
     ap.add_argument("--bf16-out", action="store_true",
                     help="d_q, d_w and d_k written as bf16 (the fp32 results rounded)")
+    ap.add_argument("--forward", action="store_true",
+                    help="time the step before the backward instead: indexer scores over every "
+                         "key plus the top-k selection, at the workload's shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample")
@@ -55,6 +58,9 @@ def main():
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.forward:
+        forward_main(args)
+        return
     import numpy as np
     import torch
 
@@ -229,6 +235,148 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def forward_main(args):
+    """The indexer forward scores (every key; causal for the dense workload) and
+    the top-k selection of the workload's topk (S_k/2 for the dense workload),
+    timed like the backward: W untimed steps, K timed steps on one stream with
+    HIP events around each step and after each kernel."""
+    import numpy as np
+    import torch
+
+    import dsa_lightning_indexer_bwd_amd as ibwd
+    from synth import WORKLOADS, make_inputs
+
+    ibwd.library()
+    wl = WORKLOADS[args.workload]
+    if args.topk:
+        wl = dataclasses.replace(wl, topk=args.topk)
+    topk = wl.S_k // 2 if wl.dense else wl.topk
+    dev = torch.device("cuda:0")
+    print("bench: generating %s inputs" % wl.name, file=sys.stderr, flush=True)
+    x = make_inputs(wl, device=dev)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k = bf16(x.q), bf16(x.k)
+    w = torch.from_numpy(x.w).to(dev)
+    B, S_q, H, D = x.q.shape
+    S_k = x.k.shape[1]
+    causal = bool(wl.dense)
+    scores = torch.empty((B, S_q, S_k), dtype=torch.float32, device=dev)
+    ids = torch.empty((B, S_q, topk), dtype=torch.int32, device=dev)
+    vals = torch.empty((B, S_q, topk), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step():
+        ibwd.indexer_fwd_scores(q, k, w, scores, causal=causal, q_offset=wl.q_offset, stream=stream)
+        ibwd.indexer_topk(scores, topk, ids, vals, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stage_events = []
+
+    def hook(stage, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        stage_events[-1].append((name, e))
+
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    ibwd.set_stage_hook(hook)
+    torch.cuda.synchronize()
+    t_all0.record(stream)
+    for e0, e1 in calls:
+        e0.record(stream)
+        stage_events.append([])
+        step()
+        e1.record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    ibwd.set_stage_hook(None)
+    per_call_ms = [e0.elapsed_time(e1) for e0, e1 in calls]
+    med_us = statistics.median(per_call_ms) * 1e3
+    # (query, key) pairs scored: every key, or the causal triangle
+    t = np.arange(S_q, dtype=np.int64)
+    pairs = B * int(np.clip(t + wl.q_offset + 1, 0, S_k).sum()) if causal else B * S_q * S_k
+    flops = 2 * pairs * H * D
+    per_kernel = {}
+    for (e0, _), evs in zip(calls, stage_events):
+        prev = e0
+        for name, e in evs:
+            per_kernel.setdefault(name, []).append(prev.elapsed_time(e) * 1e3)
+            prev = e
+    kernels = []
+    for name in ("fwd_scores_kernel", "topk_kernel"):
+        ts = per_kernel[name]
+        mean_k = statistics.fmean(ts)
+        if name == "fwd_scores_kernel":
+            work, unit, peak = flops, "TFLOP/s", PEAK_BF16_TFLOPS
+            ach = work / (mean_k * 1e-6) / 1e12
+        else:
+            # scores read once, ids and values written once
+            work, unit, peak = B * S_q * (S_k * 4 + topk * 8), "GB/s", PEAK_HBM_GBS
+            ach = work / (mean_k * 1e-6) / 1e9
+        kernels.append({"kernel": name, "us_mean": round(mean_k, 2),
+                        "us_median": round(statistics.median(ts), 2),
+                        "bound": "mfma" if unit == "TFLOP/s" else "hbm", "algorithmic_work": work,
+                        "achieved": round(ach, 3), "peak": peak, "unit": unit,
+                        "frac": round(ach / peak, 4)})
+    dom = max(kernels, key=lambda r: r["us_mean"])
+    tflops = flops / (med_us * 1e-6) / 1e12
+    out = {
+        "metric": "indexer forward scores + top-k: TFLOP/s of the score GEMM over the whole step",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_all0.elapsed_time(t_all1) / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": COMPUTE_DTYPE,
+        "data": "synthetic (seeded PCG64; q,k ~N(0,1) bf16, w ~N(0,1)/8)",
+        "config": {"workload": wl.name + "-forward", "B": B, "H": H, "D": D, "S_q": S_q, "S_k": S_k,
+                   "topk": topk, "causal": causal, "q_offset": wl.q_offset},
+        "us_per_call_median": round(med_us, 2),
+        "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
+                     "unit": dom["unit"], "frac": dom["frac"], "traffic": None,
+                     "kernel": dom["kernel"], "us_mean": dom["us_mean"],
+                     "algorithmic_work": dom["algorithmic_work"]},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_forward(x, wl, topk, causal, flops, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_forward(x, wl, topk, causal, flops, seconds):
+    """The oracle's forward scores and top-k on the first rows of the workload,
+    grown until they take about `seconds`, scaled to the whole step."""
+    import numpy as np
+
+    import oracle
+
+    q = oracle.widen_bf16(x.q)
+    k = oracle.widen_bf16(x.k)
+    S_q = q.shape[1]
+    n, spent = 16, 0.0
+    while True:
+        n = min(n, S_q)
+        t0 = time.perf_counter()
+        sc = oracle.forward_scores(q[:, :n], k, x.w[:, :n], wl.q_offset if causal else None,
+                                   np.arange(n))
+        oracle.select_topk(sc, topk)
+        spent = time.perf_counter() - t0
+        if spent * 4 > seconds or n == S_q:
+            break
+        n *= 4
+    full_s = spent * S_q / n
+    return {"value": round(flops / full_s / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+            "sample": "first %d of %d query rows (scores over every key, then top-%d), %.2f s wall"
+                      % (n, S_q, topk, spent),
+            "us_per_call_extrapolated": round(full_s * 1e6, 1)}
 
 
 def kernel_model(name, wl, B, H, D, S_q, S_k, out_bytes=4):

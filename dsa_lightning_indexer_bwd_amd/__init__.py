@@ -15,6 +15,8 @@ from typing import Optional, Tuple
 __all__ = [
     "indexer_bwd_sparse",
     "indexer_bwd_dense",
+    "indexer_fwd_scores",
+    "indexer_topk",
     "indexer_bwd_workspace_bytes",
     "indexer_bwd_strerror",
     "set_stage_hook",
@@ -67,6 +69,10 @@ def library() -> ctypes.CDLL:
         lib.indexer_bwd_dense.argtypes = [vp] * 8 + [i64] * 6 + [f32, f32, ctypes.c_uint32, vp,
                                                                  ctypes.c_size_t, vp]
         lib.indexer_bwd_dense.restype = ctypes.c_int
+        lib.indexer_fwd_scores.argtypes = [vp] * 4 + [i64] * 5 + [ctypes.c_int, i64, vp]
+        lib.indexer_fwd_scores.restype = ctypes.c_int
+        lib.indexer_topk.argtypes = [vp] * 3 + [i64] * 3 + [vp]
+        lib.indexer_topk.restype = ctypes.c_int
         lib.indexer_bwd_workspace_bytes.argtypes = [ctypes.c_int] + [i64] * 6 + [ctypes.c_uint32]
         lib.indexer_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.indexer_bwd_strerror.argtypes = [ctypes.c_int]
@@ -220,3 +226,48 @@ def indexer_bwd_dense(q, k, w, index_score, attn_score, d_q=None, d_w=None, d_k=
     if st != IBWD_OK:
         raise IndexerBwdError(st)
     return d_q, d_w, d_k
+
+
+def indexer_fwd_scores(q, k, w, scores=None, *, causal: bool = False, q_offset: int = 0,
+                       stream=None):
+    """Indexer scores [B,S_q,S_k] fp32: sum_h w*relu(q.k) for every key; with
+    causal, keys s > t + q_offset score -inf.  q [B,S_q,H,D] bf16, k [B,S_k,D]
+    bf16, w [B,S_q,H] fp32."""
+    torch = _torch()
+    B, S_q, H, D = q.shape
+    S_k = k.shape[1]
+    _check(q, torch.bfloat16, (B, S_q, H, D), "q")
+    _check(k, torch.bfloat16, (B, S_k, D), "k")
+    _check(w, torch.float32, (B, S_q, H), "w")
+    if scores is None:
+        scores = torch.empty((B, S_q, S_k), dtype=torch.float32, device=q.device)
+    _check(scores, torch.float32, (B, S_q, S_k), "scores")
+    st = library().indexer_fwd_scores(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), B, S_q, S_k, H, D,
+                                      int(bool(causal)), int(q_offset),
+                                      _stream_handle(stream, q.device))
+    if st != IBWD_OK:
+        raise IndexerBwdError(st)
+    return scores
+
+
+def indexer_topk(scores, topk: int, ids=None, values=None, *, stream=None):
+    """Top-k of each row of scores [..., S_k] fp32: (ids int32, values fp32), each
+    [..., topk]; ids ascending with -1 after the selected keys, values -inf there."""
+    torch = _torch()
+    S_k = scores.shape[-1]
+    lead = tuple(scores.shape[:-1])
+    rows = 1
+    for n in lead:
+        rows *= n
+    _check(scores, torch.float32, lead + (S_k,), "scores")
+    if ids is None:
+        ids = torch.empty(lead + (topk,), dtype=torch.int32, device=scores.device)
+    if values is None:
+        values = torch.empty(lead + (topk,), dtype=torch.float32, device=scores.device)
+    _check(ids, torch.int32, lead + (topk,), "ids")
+    _check(values, torch.float32, lead + (topk,), "values")
+    st = library().indexer_topk(_ptr(scores), _ptr(ids), _ptr(values), rows, S_k, int(topk),
+                                _stream_handle(stream, scores.device))
+    if st != IBWD_OK:
+        raise IndexerBwdError(st)
+    return ids, values

@@ -10,7 +10,7 @@ LIB_NAME = "libdsa_indexer_bwd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 HIP_SOURCES = ["indexer_bwd_kernels.hip", "indexer_bwd_rows.hip", "indexer_bwd_rows_export.hip",
-               "indexer_bwd_dk.hip"]
+               "indexer_bwd_dk.hip", "indexer_fwd.hip"]
 HOST_SOURCES = ["indexer_bwd_api.cpp"]
 
 # Device code: gfx950 only; packed-fp32 VALU forms disabled (they are formed
@@ -18,7 +18,8 @@ HOST_SOURCES = ["indexer_bwd_api.cpp"]
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # The range kernel's MFMA accumulators are consumed by VALU right away: keep
 # them in VGPRs (the default AGPR form costs a copy per accumulator register).
-PER_FILE_FLAGS = {"indexer_bwd_dk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+PER_FILE_FLAGS = {"indexer_bwd_dk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                  "indexer_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 

@@ -8,6 +8,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "fwd_launch.h"
 #include "launch.h"
 
 namespace {
@@ -167,6 +168,52 @@ size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_
   if (D != 32 && D != 64 && D != 128) return 0;
   if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, row_len)) return 0;
   return workspace_bytes(B, S_q, S_k, H, D, row_len, flags);
+}
+
+int indexer_fwd_scores(const void* q, const void* k, const float* w, float* scores, int64_t B,
+                       int64_t S_q, int64_t S_k, int64_t H, int64_t D, int causal,
+                       int64_t q_offset, hipStream_t stream) {
+  if (!q || !k || !w || !scores) return IBWD_ERR_INVALID_ARGUMENT;
+  if (B < 1 || S_q < 1 || S_k < 1 || H < 1 || H > ibwd::kMaxHeads) return IBWD_ERR_INVALID_ARGUMENT;
+  if (D != 32 && D != 64 && D != 128) return IBWD_ERR_INVALID_ARGUMENT;
+  if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, S_k)) return IBWD_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(scores, 4))
+    return IBWD_ERR_INVALID_ARGUMENT;
+  if (q_offset < -(int64_t(1) << 40) || q_offset > (int64_t(1) << 40)) return IBWD_ERR_INVALID_ARGUMENT;
+  const int st = device_status();
+  if (st != IBWD_OK) return st;
+  ibwd::FwdProblem P{};
+  P.q = static_cast<const uint16_t*>(q);
+  P.k = static_cast<const uint16_t*>(k);
+  P.w = w;
+  P.scores = scores;
+  P.B = B;
+  P.S_q = S_q;
+  P.S_k = S_k;
+  P.H = H;
+  P.D = D;
+  P.causal = causal != 0;
+  P.q_offset = q_offset;
+  return ibwd::launch_fwd_scores(P, stream) == hipSuccess ? IBWD_OK : IBWD_ERR_HIP;
+}
+
+int indexer_topk(const float* scores, int32_t* topk_ids, float* topk_scores, int64_t rows,
+                 int64_t S_k, int64_t topk, hipStream_t stream) {
+  if (!scores || !topk_ids) return IBWD_ERR_INVALID_ARGUMENT;
+  if (rows < 1 || S_k < 1 || topk < 1 || topk > S_k) return IBWD_ERR_INVALID_ARGUMENT;
+  if (!fits(rows, S_k) || !fits(rows, topk)) return IBWD_ERR_INVALID_ARGUMENT;
+  if (!aligned(scores, 4) || !aligned(topk_ids, 4) || !aligned(topk_scores, 4))
+    return IBWD_ERR_INVALID_ARGUMENT;
+  const int st = device_status();
+  if (st != IBWD_OK) return st;
+  ibwd::TopkProblem P{};
+  P.scores = scores;
+  P.ids = topk_ids;
+  P.vals = topk_scores;
+  P.rows = rows;
+  P.S_k = S_k;
+  P.topk = topk;
+  return ibwd::launch_topk(P, stream) == hipSuccess ? IBWD_OK : IBWD_ERR_HIP;
 }
 
 const char* indexer_bwd_strerror(int status) {

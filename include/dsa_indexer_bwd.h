@@ -153,6 +153,36 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
 size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_k, int64_t H,
                                    int64_t D, int64_t topk, uint32_t flags);
 
+/*
+ * indexer_fwd_scores — the indexer scores that the top-k step selects from:
+ *     scores[b,t,s] = sum_h w[b,t,h] * relu(q[b,t,h,:] . k[b,s,:])
+ * for every key s of the batch (the score whose gradients the PR #730
+ * harness's fp64 reference computes; bf16 products, fp32 accumulation).  With
+ * causal != 0, key s is visible to query t only when s <= t + q_offset, and
+ * the other keys score -inf.
+ *
+ *   q [B,S_q,H,D] bf16, k [B,S_k,D] bf16, w [B,S_q,H] fp32 (as above)
+ *   scores       [B,S_q,S_k] fp32, overwritten in full
+ * Shapes as for the backward (H <= 64, D in {32, 64, 128}); B*S_q*S_k below
+ * 2^31.  No workspace.  Returns IBWD_OK or an IBWD_ERR_* code.
+ */
+int indexer_fwd_scores(const void* q, const void* k, const float* w, float* scores, int64_t B,
+                       int64_t S_q, int64_t S_k, int64_t H, int64_t D, int causal,
+                       int64_t q_offset, hipStream_t stream);
+
+/*
+ * indexer_topk — per row of scores [rows, S_k] fp32: the min(topk, n) largest
+ * of its n finite scores (a tie at the threshold goes to the lower key id),
+ * written to topk_ids [rows, topk] int32 in ascending key id, followed by -1
+ * for the slots left over; topk_scores [rows, topk] fp32 (may be NULL)
+ * receives the selected scores and -inf after them.  -0 and +0 rank equal.
+ * 1 <= topk <= S_k; rows*S_k below 2^31; pointers 4-byte aligned.  With rows
+ * = B*S_q, the outputs are the topk_ids and index_score arguments of
+ * indexer_bwd_sparse.  No workspace.
+ */
+int indexer_topk(const float* scores, int32_t* topk_ids, float* topk_scores, int64_t rows,
+                 int64_t S_k, int64_t topk, hipStream_t stream);
+
 /* indexer_bwd_strerror — static text for a status code (never NULL). */
 const char* indexer_bwd_strerror(int status);
 

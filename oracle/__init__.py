@@ -209,14 +209,15 @@ class Problem:
 # ---------------------------------------------------------------------------
 # the step before the backward: indexer forward scores and top-k selection
 
-def forward_scores(q, k, w, q_offset: Optional[int] = None) -> np.ndarray:
+def forward_scores(q, k, w, q_offset: Optional[int] = None, t_index=None) -> np.ndarray:
     """Indexer scores I [B,S_q,S_k] in fp64: I[t,s] = sum_h w[t,h]*relu(q[t,h,:].k[s,:]).
 
     This is the score whose gradients the fp64 `ref_grads` reference of the
     NVIDIA/cudnn-frontend PR #730 benchmark harness computes (its dW is the
     sum of g*relu(S), so dI/dw = relu(S)).  q_offset None: every key of the
     batch; otherwise key s is visible to query t iff s <= t + q_offset (the
-    dense causal variant's rule) and masked keys score -inf.
+    dense causal variant's rule) and masked keys score -inf.  t_index: the
+    query index t of each row of q and w (default 0..S_q-1), for sampled rows.
     """
     q, k, w = _d(q), _d(k), _d(w)
     B, S_q, H, D = q.shape
@@ -226,7 +227,7 @@ def forward_scores(q, k, w, q_offset: Optional[int] = None) -> np.ndarray:
         S = np.matmul(q[b], k[b].T)                          # [S_q,H,S_k]
         out[b] = np.einsum("th,ths->ts", w[b], np.maximum(S, 0.0))
     if q_offset is not None:
-        t = np.arange(S_q)[:, None]
+        t = (np.arange(S_q) if t_index is None else np.asarray(t_index))[:, None]
         s = np.arange(S_k)[None, :]
         out[:, s > t + q_offset] = -np.inf
     return out

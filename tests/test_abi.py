@@ -123,3 +123,40 @@ def test_stage_hook_set_and_remove_without_gpu():
         ibwd.set_stage_hook(None)
     assert seen == []
     assert ibwd.library().indexer_bwd_set_stage_hook(ibwd._HOOK_T(), None) == ibwd.IBWD_OK
+
+
+def test_forward_and_topk_reject_invalid_arguments():
+    lib = ibwd.library()
+    q, k, w, sc = A, A + 0x100000, A + 0x200000, A + 0x300000
+
+    def fwd(**kw):
+        a = dict(q=q, k=k, w=w, sc=sc, B=1, S_q=16, S_k=64, H=4, D=32, causal=0, off=0)
+        a.update(kw)
+        return lib.indexer_fwd_scores(a["q"], a["k"], a["w"], a["sc"], a["B"], a["S_q"], a["S_k"],
+                                      a["H"], a["D"], a["causal"], a["off"], None)
+
+    for bad in (dict(q=None), dict(k=None), dict(w=None), dict(sc=None), dict(B=0), dict(S_k=0),
+                dict(H=65), dict(D=48), dict(q=A + 8), dict(sc=A + 0x300002), dict(off=1 << 41),
+                dict(S_q=1 << 16, S_k=1 << 16)):
+        assert fwd(**bad) == ibwd.IBWD_ERR_INVALID_ARGUMENT, bad
+
+    def topk(**kw):
+        a = dict(sc=sc, ids=A + 0x400000, vals=A + 0x500000, rows=8, S_k=64, topk=16)
+        a.update(kw)
+        return lib.indexer_topk(a["sc"], a["ids"], a["vals"], a["rows"], a["S_k"], a["topk"], None)
+
+    for bad in (dict(sc=None), dict(ids=None), dict(rows=0), dict(S_k=0), dict(topk=0),
+                dict(topk=65), dict(ids=A + 0x400002), dict(vals=A + 0x500001),
+                dict(rows=1 << 20, S_k=1 << 12)):
+        assert topk(**bad) == ibwd.IBWD_ERR_INVALID_ARGUMENT, bad
+
+
+def test_forward_and_topk_without_gpu_fail_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: covered by the GPU tests")
+    lib = ibwd.library()
+    assert lib.indexer_fwd_scores(A, A + 0x100000, A + 0x200000, A + 0x300000, 1, 16, 64, 4, 32, 1,
+                                  0, None) in (ibwd.IBWD_ERR_HIP, ibwd.IBWD_ERR_UNSUPPORTED_DEVICE)
+    assert lib.indexer_topk(A, A + 0x400000, None, 8, 64, 16, None) in (
+        ibwd.IBWD_ERR_HIP, ibwd.IBWD_ERR_UNSUPPORTED_DEVICE)
