@@ -7,8 +7,9 @@
 //                      the query's q in registers and 64-key K tiles in LDS
 //                      shared by the 8 waves, then I = sum_h w * relu(S)
 //   topk_kernel        one workgroup per query row: radix select of the k-th
-//                      largest finite score (four 8-bit passes over an
-//                      order-preserving key), then an id-ordered compaction
+//                      largest finite score (8-bit passes over an order-
+//                      preserving key, from the highest bit in which the
+//                      row's keys differ), then an id-ordered compaction
 //
 // The score is the one whose gradients the fp64 reference of the
 // NVIDIA/cudnn-frontend PR #730 benchmark harness computes (its dW is the sum
@@ -184,22 +185,24 @@ hipError_t launch_fwd_t(const FwdProblem& P, hipStream_t stream) {
 
 // ---- top-k selection -------------------------------------------------------------
 
-// Order-preserving unsigned key of a float (larger float, larger key); -0
-// ranks with +0.
-__device__ __forceinline__ uint32_t order_key(float f) {
+// Order-preserving unsigned key of a finite float (larger float, larger key;
+// -0 ranks with +0); every finite float maps to at least 0x00800000, so 0
+// marks a score that is not a candidate (+-inf, NaN).
+__device__ __forceinline__ uint32_t cand_key(float f) {
   uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return 0u;
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ bool is_finite(float f) {
-  return (__float_as_uint(f) & 0x7f800000u) != 0x7f800000u;
-}
 
+// One workgroup per row.  E > 0: the row (at most 256*E scores) is read once
+// into registers, thread tid holding ids tid + 256u; E == 0: every pass reads
+// the row again.
+template <int E>
 __global__ __launch_bounds__(256) void topk_kernel(TopkProblem P) {
-  __shared__ int hist[4][256];   // one histogram per wave
-  __shared__ int part[4];
-  __shared__ int part2[4];
-  __shared__ uint32_t s_sel[2];  // bin found, count above it
+  __shared__ int hist[4][256];  // one histogram per wave
+  __shared__ uint32_t part[3][4];
+  __shared__ uint32_t s_sel[2];  // digit found, count of candidates above it
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -210,102 +213,124 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkProblem P) {
   int32_t* ids = P.ids + r * P.topk;
   float* vals = P.vals ? P.vals + r * P.topk : nullptr;
 
-  // block-wide sums of two per-thread counts (all threads get both totals)
-  auto block_sum2 = [&](int x, int y, int& sx, int& sy) {
+  uint32_t kreg[E > 0 ? E : 1];
+  if (E > 0) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      x += __shfl_xor(x, o, 64);
-      y += __shfl_xor(y, o, 64);
+    for (int u = 0; u < E; ++u) {
+      const int s = tid + 256 * u;
+      kreg[u] = s < S_k ? cand_key(row[s]) : 0u;
     }
-    if (lane == 0) {
-      part[wave] = x;
-      part2[wave] = y;
+  }
+  // f(s, key) for each of this thread's ids s = tid + 256u (key 0: not a candidate)
+  auto for_each = [&](auto f) {
+    if (E > 0) {
+#pragma unroll
+      for (int u = 0; u < (E > 0 ? E : 1); ++u) f(tid + 256 * u, kreg[u]);
+    } else {
+      for (int s = tid; s < S_k; s += 256) f(s, cand_key(row[s]));
     }
-    __syncthreads();
-    sx = part[0] + part[1] + part[2] + part[3];
-    sy = part2[0] + part2[1] + part2[2] + part2[3];
-    __syncthreads();
   };
 
-  uint32_t prefix = 0u, mask = 0u;
-  int krem = 0;  // after the passes: how many keys equal to the threshold to take
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
-    __syncthreads();
-    int nfin = 0;
-    for (int s = tid; s < S_k; s += 256) {
-      const float f = row[s];
-      if (!is_finite(f)) continue;
+  // candidates, and the smallest and largest candidate key
+  uint32_t kmin = 0xffffffffu, kmax = 0u, nfin = 0u;
+  for_each([&](int, uint32_t key) {
+    if (key) {
       ++nfin;
-      const uint32_t key = order_key(f);
-      if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1);
+      kmin = key < kmin ? key : kmin;
+      kmax = key > kmax ? key : kmax;
     }
-    __syncthreads();
-    if (pass == 0) {
-      int total, unused;
-      block_sum2(nfin, 0, total, unused);
-      krem = total < topk ? total : topk;
-      if (krem == 0) break;
-    }
-    // bins in descending order: thread i holds bin 255 - i; inclusive scan
-    const int bin = 255 - tid;
-    const int c = hist[0][bin] + hist[1][bin] + hist[2][bin] + hist[3][bin];
-    int incl = c;
+  });
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
+  for (int o = 32; o >= 1; o >>= 1) {
+    nfin += uint32_t(__shfl_xor(int(nfin), o, 64));
+    const uint32_t a = uint32_t(__shfl_xor(int(kmin), o, 64));
+    const uint32_t c = uint32_t(__shfl_xor(int(kmax), o, 64));
+    kmin = a < kmin ? a : kmin;
+    kmax = c > kmax ? c : kmax;
+  }
+  if (lane == 0) {
+    part[0][wave] = nfin;
+    part[1][wave] = kmin;
+    part[2][wave] = kmax;
+  }
+  __syncthreads();
+  nfin = part[0][0] + part[0][1] + part[0][2] + part[0][3];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    kmin = part[1][w] < kmin ? part[1][w] : kmin;
+    kmax = part[2][w] > kmax ? part[2][w] : kmax;
+  }
+  __syncthreads();
+  const int keff = int(nfin) < topk ? int(nfin) : topk;
+
+  // radix select of the keff-th largest key over the bits below the highest
+  // bit in which the candidates differ (all candidates share the bits above)
+  int krem = keff;  // then: how many keys equal to the threshold to take
+  uint32_t prefix = kmax;
+  if (keff > 0 && kmin != kmax) {
+    int lo = 32 - __builtin_clz(kmin ^ kmax);  // undecided low bits
+    prefix = lo == 32 ? 0u : (kmax >> lo) << lo;
+    while (lo > 0) {
+      const int shift = lo > 8 ? lo - 8 : 0;
+      const int width = lo - shift;
+      for (int i = tid; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
+      __syncthreads();
+      for_each([&](int, uint32_t key) {
+        if (key && (lo == 32 || (key >> lo) == (prefix >> lo)))
+          atomicAdd(&hist[wave][(key >> shift) & ((1u << width) - 1u)], 1);
+      });
+      __syncthreads();
+      // digits in descending order: thread i holds digit (2^width - 1 - i); inclusive scan
+      const int digit = (1 << width) - 1 - tid;
+      const int c = digit >= 0 ? hist[0][digit] + hist[1][digit] + hist[2][digit] + hist[3][digit] : 0;
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      if (lane == 63) part[0][wave] = uint32_t(incl);
+      __syncthreads();
+      for (int w = 0; w < wave; ++w) incl += int(part[0][w]);
+      if (c > 0 && incl >= krem && incl - c < krem) {
+        s_sel[0] = uint32_t(digit);
+        s_sel[1] = uint32_t(incl - c);
+      }
+      __syncthreads();
+      prefix |= s_sel[0] << shift;
+      krem -= int(s_sel[1]);
+      lo = shift;
+      __syncthreads();
     }
-    if (lane == 63) part[wave] = incl;
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) incl += part[w];
-    if (incl >= krem && incl - c < krem) {
-      s_sel[0] = uint32_t(bin);
-      s_sel[1] = uint32_t(incl - c);
-    }
-    __syncthreads();
-    prefix |= s_sel[0] << shift;
-    mask |= 0xffu << shift;
-    krem -= int(s_sel[1]);
-    __syncthreads();
   }
 
+  // prefix is the keff-th largest key: write every larger key and the first
+  // krem keys equal to it, in ascending id order
   int nsel = 0;
-  if (krem > 0) {  // at least one finite score
-    // prefix is the k-th largest key; take every larger key and the first
-    // krem keys equal to it, in ascending id order
+  if (keff > 0) {
     const uint32_t thr = prefix;
     const int keq = krem;
     int gt_run = 0, eq_run = 0;
-    for (int s0 = 0; s0 < S_k; s0 += 256) {
-      const int s = s0 + tid;
-      float f = 0.f;
-      bool gt = false, eq = false;
-      if (s < S_k) {
-        f = row[s];
-        if (is_finite(f)) {
-          const uint32_t key = order_key(f);
-          gt = key > thr;
-          eq = key == thr;
-        }
-      }
+    // ids 256u .. 256u + 255 in one step: thread tid holds id s = 256u + tid
+    auto step = [&](int s, uint32_t key) {
+      const bool gt = key > thr;
+      const bool eq = key != 0u && key == thr;
       const uint64_t mg = ballot(gt);
       const uint64_t me = ballot(eq);
       if (lane == 0) {
-        part[wave] = __popcll(mg);
-        part2[wave] = __popcll(me);
+        part[0][wave] = uint32_t(__popcll(mg));
+        part[1][wave] = uint32_t(__popcll(me));
       }
       __syncthreads();
       int gb = gt_run, eb = eq_run, gtot = 0, etot = 0;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         if (w < wave) {
-          gb += part[w];
-          eb += part2[w];
+          gb += int(part[0][w]);
+          eb += int(part[1][w]);
         }
-        gtot += part[w];
-        etot += part2[w];
+        gtot += int(part[0][w]);
+        etot += int(part[1][w]);
       }
       __syncthreads();
       gb += __popcll(mg & lanemask_lt());
@@ -313,10 +338,21 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkProblem P) {
       if (gt || (eq && eb < keq)) {
         const int pos = gb + (eb < keq ? eb : keq);
         ids[pos] = s;
-        if (vals) vals[pos] = f;
+        if (vals) vals[pos] = row[s];
       }
       gt_run += gtot;
       eq_run += etot;
+    };
+    const int rounds = (S_k + 255) / 256;
+    if (E > 0) {
+#pragma unroll
+      for (int u = 0; u < (E > 0 ? E : 1); ++u)
+        if (u < rounds) step(tid + 256 * u, kreg[u]);
+    } else {
+      for (int u = 0; u < rounds; ++u) {
+        const int s = tid + 256 * u;
+        step(s, s < S_k ? cand_key(row[s]) : 0u);
+      }
     }
     nsel = gt_run + (eq_run < keq ? eq_run : keq);
   }
@@ -342,7 +378,15 @@ hipError_t launch_fwd_scores(const FwdProblem& P, hipStream_t stream) {
 }
 
 hipError_t launch_topk(const TopkProblem& P, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_kernel, dim3(unsigned(P.rows)), dim3(256), 0, stream, P);
+  const dim3 grid(unsigned(P.rows));
+  if (P.S_k <= 1024)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, stream, P);
+  else if (P.S_k <= 2048)
+    hipLaunchKernelGGL(topk_kernel<8>, grid, dim3(256), 0, stream, P);
+  else if (P.S_k <= 4096)
+    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, stream, P);
+  else
+    hipLaunchKernelGGL(topk_kernel<0>, grid, dim3(256), 0, stream, P);
   const hipError_t err = hipGetLastError();
   if (err == hipSuccess) stage_done(0, "topk_kernel");
   return err;

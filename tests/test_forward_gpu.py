@@ -121,12 +121,14 @@ def test_topk_of_forward_scores(ibwd, topk):
     assert (ids[:, 0, min(topk, 21):] == -1).all()
 
 
-def test_topk_ties_signed_zero_and_non_finite(ibwd):
+@pytest.mark.parametrize("S_k", [1000, 2000, 4096, 5000])
+def test_topk_ties_signed_zero_and_non_finite(ibwd, S_k):
     """Heavy ties (values on a coarse grid), +0 and -0, -inf, +inf and NaN (not
-    candidates), all-masked rows and rows longer than one pass of the block."""
-    log("case: topk ties and special values")
+    candidates), all-masked rows, a row of equal values; rows held in registers
+    (S_k <= 4096, three sizes) and rows read from memory per pass (5000)."""
+    log(f"case: topk ties and special values S_k={S_k}")
     rng = np.random.default_rng(7)
-    rows, S_k = 24, 5000
+    rows = 24
     x = (np.round(rng.standard_normal((rows, S_k)) * 2) / 2).astype(np.float32)
     x[rng.random(x.shape) < 0.1] = -np.inf
     x[rng.random(x.shape) < 0.02] = np.inf
@@ -136,8 +138,11 @@ def test_topk_ties_signed_zero_and_non_finite(ibwd):
     x[4, :] = 0.0
     x[4, ::3] = -0.0
     x[5, 7:] = np.nan
+    x[6, :] = 1.5                     # every key equal
+    x[7, :] = np.float32(3.0e38)      # equal and near the largest float
+    x[7, ::5] = -np.float32(3.0e38)
     sc = torch.from_numpy(x).cuda()
-    for topk in (1, 64, 1000, 4999, 5000):
+    for topk in (1, 64, S_k // 2, S_k - 1, S_k):
         check_topk(ibwd, sc, topk)
 
 
