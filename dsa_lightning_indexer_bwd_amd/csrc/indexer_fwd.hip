@@ -4,7 +4,7 @@
 //
 //   fwd_scores_kernel  one workgroup of 8 waves per 8 queries of a batch, one
 //                      query per wave: S = q.k^T on bf16 MFMA (32x32x16) with
-//                      the query's q in registers and 64-key K tiles in LDS
+//                      the query's q in registers and 256-key K tiles in LDS
 //                      shared by the 8 waves, then I = sum_h w * relu(S)
 //   topk_kernel        one workgroup per query row: radix select of the k-th
 //                      largest finite score (8-bit passes over an order-
@@ -28,7 +28,7 @@ namespace {
 constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdQB = kFwdWaves;  // queries per workgroup, one per wave
-constexpr int kFwdNK = 64;         // keys per LDS tile
+constexpr int kFwdNK = 256;        // keys per LDS tile
 
 // LDS K tile [kFwdNK][D] bf16.  A B-operand read has 16 lanes fetch the same
 // 16-byte chunk of 16 consecutive key rows; the chunk index is XORed with the
@@ -179,6 +179,9 @@ hipError_t launch_fwd_t(const FwdProblem& P, hipStream_t stream) {
   const size_t lds = 2 * FwdTile<D>::kBytes + kFwdQB * NMT * 32 * sizeof(float);
   const int64_t nqb = (P.S_q + kFwdQB - 1) / kFwdQB;
   const dim3 grid(unsigned(P.B * nqb));
+  const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_scores_kernel<D, NMT>),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((fwd_scores_kernel<D, NMT>), grid, dim3(kFwdThreads), lds, stream, P);
   return hipGetLastError();
 }
