@@ -125,6 +125,11 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_scores_kernel(FwdProblem P) {
   const int64_t vis = P.causal ? tq + P.q_offset : int64_t(S_k) - 1;  // last visible key
   const bool store = tq < P.S_q && half == 0;
   const float* wq = wl + wave * NMT * 32 + 4 * half;
+  float4 wr[NMT][4];  // w of this lane's heads 32mt + 8i + 4*half + (0..3)
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[mt][i] = *reinterpret_cast<const float4*>(wq + 32 * mt + 8 * i);
 
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_scores_kernel(FwdProblem P) {
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float4 w4 = *reinterpret_cast<const float4*>(wq + 32 * mt + 8 * i);
+          const float4 w4 = wr[mt][i];
           v += w4.x * fmaxf(acc[mt][4 * i + 0], 0.f);
           v += w4.y * fmaxf(acc[mt][4 * i + 1], 0.f);
           v += w4.z * fmaxf(acc[mt][4 * i + 2], 0.f);
