@@ -70,6 +70,8 @@ def check_scores(got, q64, k64, w, q_offset, t_index=None):
     (1, 17, 130, 8, 32, True, -5),       # negative offset: the first rows see no key
     (1, 64, 512, 64, 128, True, 100),
     (3, 9, 65, 1, 32, False, 0),         # one head; one key past a tile
+    (1, 24, 700, 40, 32, True, 3),       # D=32 with two head tiles; keys past a 256-key tile
+    (2, 16, 1000, 20, 128, False, 0),    # D=128 with one head tile
 ])
 def test_fwd_scores_small(ibwd, B, S_q, S_k, H, D, causal, q_offset):
     log(f"case: fwd scores B={B} S_q={S_q} S_k={S_k} H={H} D={D} causal={causal} off={q_offset}")
