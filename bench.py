@@ -274,6 +274,13 @@ def forward_main(args):
         ibwd.indexer_fwd_scores(q, k, w, scores, causal=causal, q_offset=wl.q_offset, stream=stream)
         ibwd.indexer_topk(scores, topk, ids, vals, stream=stream)
 
+    if args.calibration_copy_mib:
+        src = torch.ones(args.calibration_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -340,7 +347,9 @@ def forward_main(args):
         "us_per_call_median": round(med_us, 2),
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
-                     "unit": dom["unit"], "frac": dom["frac"], "traffic": None,
+                     "unit": dom["unit"], "frac": dom["frac"],
+                     "traffic": None if args.topk else measured_traffic(dom["kernel"],
+                                                                       wl.name + "-forward", False),
                      "kernel": dom["kernel"], "us_mean": dom["us_mean"],
                      "algorithmic_work": dom["algorithmic_work"]},
         "kernels": kernels,
