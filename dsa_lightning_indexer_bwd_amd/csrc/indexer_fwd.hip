@@ -211,6 +211,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkProblem P) {
   __shared__ int hist[4][256];  // one histogram per wave
   __shared__ uint32_t part[3][4];
   __shared__ uint32_t s_sel[2];  // digit found, count of candidates above it
+  __shared__ int4 cnt[E > 0 ? E : 1][2];  // per 256-id round: above / equal counts of each wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -221,12 +222,14 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkProblem P) {
   int32_t* ids = P.ids + r * P.topk;
   float* vals = P.vals ? P.vals + r * P.topk : nullptr;
 
-  uint32_t kreg[E > 0 ? E : 1];
+  uint32_t kreg[E > 0 ? E : 1];   // keys
+  float freg[E > 0 ? E : 1];      // the scores themselves, for the output values
   if (E > 0) {
 #pragma unroll
     for (int u = 0; u < E; ++u) {
       const int s = tid + 256 * u;
-      kreg[u] = s < S_k ? cand_key(row[s]) : 0u;
+      freg[u] = s < S_k ? row[s] : 0.f;
+      kreg[u] = s < S_k ? cand_key(freg[u]) : 0u;
     }
   }
   // f(s, key) for each of this thread's ids s = tid + 256u (key 0: not a candidate)
@@ -353,9 +356,42 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkProblem P) {
     };
     const int rounds = (S_k + 255) / 256;
     if (E > 0) {
+      // the row is in registers: every round's per-wave counts first, then one
+      // barrier, then each thread's output positions from those counts (no
+      // load and no barrier between the stores)
+      const uint64_t lt = lanemask_lt();
 #pragma unroll
-      for (int u = 0; u < (E > 0 ? E : 1); ++u)
-        if (u < rounds) step(tid + 256 * u, kreg[u]);
+      for (int u = 0; u < (E > 0 ? E : 1); ++u) {
+        const uint64_t mg = ballot(kreg[u] > thr);
+        const uint64_t me = ballot(kreg[u] != 0u && kreg[u] == thr);
+        if (lane == 0) {
+          reinterpret_cast<int*>(&cnt[u][0])[wave] = __popcll(mg);
+          reinterpret_cast<int*>(&cnt[u][1])[wave] = __popcll(me);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < (E > 0 ? E : 1); ++u) {
+        if (u >= rounds) break;
+        const int4 g4 = cnt[u][0];
+        const int4 e4 = cnt[u][1];
+        const uint32_t key = kreg[u];
+        const bool gt = key > thr;
+        const bool eq = key != 0u && key == thr;
+        const uint64_t mg = ballot(gt);
+        const uint64_t me = ballot(eq);
+        const int gb = gt_run + (wave > 0 ? g4.x : 0) + (wave > 1 ? g4.y : 0) + (wave > 2 ? g4.z : 0) +
+                       __popcll(mg & lt);
+        const int eb = eq_run + (wave > 0 ? e4.x : 0) + (wave > 1 ? e4.y : 0) + (wave > 2 ? e4.z : 0) +
+                       __popcll(me & lt);
+        if (gt || (eq && eb < keq)) {
+          const int pos = gb + (eb < keq ? eb : keq);
+          ids[pos] = tid + 256 * u;
+          if (vals) vals[pos] = freg[u];
+        }
+        gt_run += g4.x + g4.y + g4.z + g4.w;
+        eq_run += e4.x + e4.y + e4.z + e4.w;
+      }
     } else {
       for (int u = 0; u < rounds; ++u) {
         const int s = tid + 256 * u;
