@@ -17,6 +17,10 @@
  *     d_k[s,:]  = sum over every (t, j in V) with id_j = s of sum_h G[h,j] * q[t,h,:]
  * (index_score is I, attn_score is the target distribution p.)
  *
+ * The step before it is declared here too: indexer_fwd_scores computes I for
+ * every key and indexer_topk selects each row's top-k, whose ids and scores
+ * are this backward's topk_ids and index_score.
+ *
  * Conventions shared by every entry point
  *   - All tensors are dense, row-major, contiguous, and live in device memory
  *     of the current HIP device.  bf16 tensors are passed as their 16-bit
