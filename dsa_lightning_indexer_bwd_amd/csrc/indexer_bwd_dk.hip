@@ -124,14 +124,20 @@ __device__ __forceinline__ void wait_vm() {
 // (it would wait for the copy before every later LDS read, the copy's own
 // destination or not) nor counts it: the kernel waits for these copies itself,
 // and the compiler's own vmcnt waits stay correct, only more conservative.
-// M0 is a reserved register, so the compiler does not save it around the
-// statement (it warns about the clobber); nothing else in this file reads M0
-// (gfx950's LDS instructions do not), and every copy sets M0 itself.
+// M0 is saved and restored inside the statement, so the compiler's view of it
+// never changes; one wait state separates the SALU write of M0 from the copy
+// that reads it (a gfx9 hazard).
 __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* gbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(gbase)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(gbase)
+      : "memory");
 }
 
 // Byte offset of chunk (16 bytes) c of row d of a Q' tile in LDS: the chunk

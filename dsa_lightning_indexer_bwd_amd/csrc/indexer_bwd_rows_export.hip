@@ -383,13 +383,17 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   // Records of chunk c are stored by the record wave in iteration c+1, after
   // the iteration's one wait and before its loads (gfx9's vmcnt counts stores
   // too, and a store issued after a load that is waited for later turns that
-  // wait into a full drain).  Only lanes of valid slots store.
+  // wait into a full drain).  Only lanes of valid slots store.  The validity
+  // comes from the dI wave's stage (its key) and the position from the prep
+  // kernel, which marks exactly the same slots (same ids, same key rule) with
+  // -1; the store still checks the position itself, so that no slot can
+  // address memory before the row's records.
   int prev_pos = 0;
   bool prev_valid = false;
   int2 prev_kd = make_int2(-1, 0);
   uint32_t prev_mask = 0u;
   auto store_records = [&](int c_prev) {
-    if (rec_wave && prev_valid) {
+    if (rec_wave && prev_valid && prev_pos >= 0) {
       const uint32_t w1 = NG == 2 ? w1x[(c_prev & 1) * kSlots + l32] : 0u;
       rkd[prev_pos] = prev_kd;
       rmask[prev_pos] = make_uint2(prev_mask, w1);
