@@ -125,33 +125,39 @@ def _check(t, dtype, shape, name):
         raise ValueError("%s must be contiguous" % name)
 
 
-def _stream_handle(stream, device) -> int:
+def _stream(stream, device):
+    """The torch stream a call runs on: the given one, else the device's current stream."""
     torch = _torch()
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return int(s.cuda_stream)
+    return torch.cuda.current_stream(device) if stream is None else stream
 
 
-def _outputs(q, k, d_q, d_w, d_k, bf16_out):
-    """The three outputs (allocated when None), checked for dtype and shape."""
+def _outputs(q, k, d_q, d_w, d_k, bf16_out, stream):
+    """The three outputs (allocated on `stream` when None), checked for dtype and shape."""
     torch = _torch()
     B, S_q, H, D = q.shape
     S_k = k.shape[1]
     dt = torch.bfloat16 if bf16_out else torch.float32
     shapes = ((B, S_q, H, D), (B, S_q, H), (B, S_k, D))
-    out = [torch.empty(s, dtype=dt, device=q.device) if t is None else t
-           for t, s in zip((d_q, d_w, d_k), shapes)]
+    with torch.cuda.stream(stream):
+        out = [torch.empty(s, dtype=dt, device=q.device) if t is None else t
+               for t, s in zip((d_q, d_w, d_k), shapes)]
     for t, s, name in zip(out, shapes, ("d_q", "d_w", "d_k")):
         _check(t, dt, s, name)
     return tuple(out)
 
 
-def _workspace(dense, B, S_q, S_k, H, D, topk, flags, workspace, device):
+def _workspace(dense, B, S_q, S_k, H, D, topk, flags, workspace, device, stream):
+    """The caller's workspace, or one allocated here.  An allocated workspace
+    belongs to the stream the kernels run on, so the caching allocator hands its
+    memory to other work only in that stream's order, after the kernels that
+    use it, even though it is released when this call returns."""
     torch = _torch()
     need = indexer_bwd_workspace_bytes(dense, B, S_q, S_k, H, D, topk, flags)
     if need == 0:
         return workspace, 0 if workspace is None else workspace.numel() * workspace.element_size()
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -187,13 +193,14 @@ def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w
     _check(topk_ids, torch.int32, (B, S_q, topk), "topk_ids")
     _check(index_score, torch.float32, (B, S_q, topk), "index_score")
     _check(attn_score, torch.float32, (B, S_q, topk), "attn_score")
-    d_q, d_w, d_k = _outputs(q, k, d_q, d_w, d_k, bf16_out)
+    s = _stream(stream, q.device)
+    d_q, d_w, d_k = _outputs(q, k, d_q, d_w, d_k, bf16_out, s)
     flags = _flags(deterministic, atomic_dk, bf16_out) | (IBWD_FLAG_GLOBAL_IDS if global_ids else 0)
-    workspace, ws_bytes = _workspace(False, B, S_q, S_k, H, D, topk, flags, workspace, q.device)
+    workspace, ws_bytes = _workspace(False, B, S_q, S_k, H, D, topk, flags, workspace, q.device, s)
     st = library().indexer_bwd_sparse(
         _ptr(q), _ptr(k), _ptr(w), _ptr(topk_ids), _ptr(index_score), _ptr(attn_score), _ptr(d_q),
         _ptr(d_w), _ptr(d_k), B, S_q, S_k, H, D, topk, float(sm_scale), float(grad_loss), flags,
-        _ptr(workspace), ws_bytes, _stream_handle(stream, q.device))
+        _ptr(workspace), ws_bytes, int(s.cuda_stream))
     if st != IBWD_OK:
         raise IndexerBwdError(st)
     return d_q, d_w, d_k
@@ -216,13 +223,14 @@ def indexer_bwd_dense(q, k, w, index_score, attn_score, d_q=None, d_w=None, d_k=
     _check(w, torch.float32, (B, S_q, H), "w")
     _check(index_score, torch.float32, (B, S_q, S_k), "index_score")
     _check(attn_score, torch.float32, (B, S_q, S_k), "attn_score")
-    d_q, d_w, d_k = _outputs(q, k, d_q, d_w, d_k, bf16_out)
+    s = _stream(stream, q.device)
+    d_q, d_w, d_k = _outputs(q, k, d_q, d_w, d_k, bf16_out, s)
     flags = _flags(deterministic, atomic_dk, bf16_out)
-    workspace, ws_bytes = _workspace(True, B, S_q, S_k, H, D, S_k, flags, workspace, q.device)
+    workspace, ws_bytes = _workspace(True, B, S_q, S_k, H, D, S_k, flags, workspace, q.device, s)
     st = library().indexer_bwd_dense(
         _ptr(q), _ptr(k), _ptr(w), _ptr(index_score), _ptr(attn_score), _ptr(d_q), _ptr(d_w),
         _ptr(d_k), B, S_q, S_k, H, D, int(q_offset), float(sm_scale), float(grad_loss), flags,
-        _ptr(workspace), ws_bytes, _stream_handle(stream, q.device))
+        _ptr(workspace), ws_bytes, int(s.cuda_stream))
     if st != IBWD_OK:
         raise IndexerBwdError(st)
     return d_q, d_w, d_k
@@ -239,12 +247,13 @@ def indexer_fwd_scores(q, k, w, scores=None, *, causal: bool = False, q_offset: 
     _check(q, torch.bfloat16, (B, S_q, H, D), "q")
     _check(k, torch.bfloat16, (B, S_k, D), "k")
     _check(w, torch.float32, (B, S_q, H), "w")
+    s = _stream(stream, q.device)
     if scores is None:
-        scores = torch.empty((B, S_q, S_k), dtype=torch.float32, device=q.device)
+        with torch.cuda.stream(s):
+            scores = torch.empty((B, S_q, S_k), dtype=torch.float32, device=q.device)
     _check(scores, torch.float32, (B, S_q, S_k), "scores")
     st = library().indexer_fwd_scores(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), B, S_q, S_k, H, D,
-                                      int(bool(causal)), int(q_offset),
-                                      _stream_handle(stream, q.device))
+                                      int(bool(causal)), int(q_offset), int(s.cuda_stream))
     if st != IBWD_OK:
         raise IndexerBwdError(st)
     return scores
@@ -260,14 +269,16 @@ def indexer_topk(scores, topk: int, ids=None, values=None, *, stream=None):
     for n in lead:
         rows *= n
     _check(scores, torch.float32, lead + (S_k,), "scores")
-    if ids is None:
-        ids = torch.empty(lead + (topk,), dtype=torch.int32, device=scores.device)
-    if values is None:
-        values = torch.empty(lead + (topk,), dtype=torch.float32, device=scores.device)
+    s = _stream(stream, scores.device)
+    with torch.cuda.stream(s):
+        if ids is None:
+            ids = torch.empty(lead + (topk,), dtype=torch.int32, device=scores.device)
+        if values is None:
+            values = torch.empty(lead + (topk,), dtype=torch.float32, device=scores.device)
     _check(ids, torch.int32, lead + (topk,), "ids")
     _check(values, torch.float32, lead + (topk,), "values")
     st = library().indexer_topk(_ptr(scores), _ptr(ids), _ptr(values), rows, S_k, int(topk),
-                                _stream_handle(stream, scores.device))
+                                int(s.cuda_stream))
     if st != IBWD_OK:
         raise IndexerBwdError(st)
     return ids, values

@@ -87,6 +87,7 @@ int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32
                         flags);
   if (st != IBWD_OK) return st;
   if (!topk_ids || !aligned(topk_ids, 4)) return IBWD_ERR_INVALID_ARGUMENT;
+  if (topk > S_k) return IBWD_ERR_INVALID_ARGUMENT;  // more slots than keys
   size_t need = workspace_bytes(B, S_q, S_k, H, D, topk, flags);
   if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256)))
     return IBWD_ERR_INVALID_ARGUMENT;
@@ -165,6 +166,7 @@ size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_
                                    int64_t D, int64_t topk, uint32_t flags) {
   const int64_t row_len = dense ? S_k : topk;
   if (B < 1 || S_q < 1 || S_k < 1 || H < 1 || H > ibwd::kMaxHeads || row_len < 1) return 0;
+  if (row_len > S_k) return 0;
   if (D != 32 && D != 64 && D != 128) return 0;
   if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, row_len)) return 0;
   return workspace_bytes(B, S_q, S_k, H, D, row_len, flags);

@@ -76,7 +76,8 @@ struct ExportLds {
   }
   // two K tiles (chunks c, c+1); at row start each wave stages its Q' in one
   static constexpr int kStageOff = 2 * kTile;
-  static constexpr int kStageBytes = kSlots * 12;  // dI (fp32), key, record position; ring of 4
+  // dI (fp32), key, record position, dI - bf16(dI) (fp32); ring of 4
+  static constexpr int kStageBytes = kSlots * 16;
   static constexpr int kW1Off = kStageOff + 4 * kStageBytes;  // sign words of wave 1, ring of 2
   static constexpr int kBytes = kW1Off + 2 * kSlots * 4;
 };
@@ -223,7 +224,10 @@ __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
   }
 }
 
-template <int D, bool DENSE, int NG>
+// SPLIT: GEMM2 takes G' as two bf16 terms, bf16(G') and bf16(G' - bf16(G')),
+// so that dQ carries only fp32 accumulation error (for bf16 outputs, whose own
+// rounding would otherwise add to that of G').
+template <int D, bool DENSE, int NG, bool SPLIT>
 __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) void row_export_kernel(
     Problem P) {
   constexpr int KD = D / 16;  // GEMM1 k-steps over d
@@ -335,8 +339,11 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int j = c * kSlots + l32;
     const int key = key_of(j, v.id);
     if (dI_wave) {
-      reinterpret_cast<float*>(stage_ptr(c))[l32] = key >= 0 ? __int_as_float(v.pd.y) : 0.f;
+      const float dI = key >= 0 ? __int_as_float(v.pd.y) : 0.f;
+      reinterpret_cast<float*>(stage_ptr(c))[l32] = dI;
       reinterpret_cast<int*>(stage_ptr(c) + kSlots * 4)[l32] = key;
+      // the part of dI that bf16(dI) drops (exact in fp32)
+      if (SPLIT) reinterpret_cast<float*>(stage_ptr(c) + kSlots * 12)[l32] = dI - bf16_lo(pack_bf16(dI, 0.f));
     }
     if (rec_wave) reinterpret_cast<int*>(stage_ptr(c) + kSlots * 8)[l32] = v.pd.x;
     return key;
@@ -429,7 +436,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     // lane: head hl; register 4*i + rr <-> slot 8*i + 4*half + rr
     const float* sd = reinterpret_cast<const float*>(stage_ptr(c));
     const int* sk = reinterpret_cast<const int*>(stage_ptr(c) + kSlots * 4);
-    float dIv[4][4];
+    float dIv[4][4], dIl[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 v = *reinterpret_cast<const float4*>(sd + 8 * i + 4 * half);
@@ -437,17 +444,25 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
       dIv[i][1] = v.y;
       dIv[i][2] = v.z;
       dIv[i][3] = v.w;
+      if (SPLIT) {
+        const float4 u = *reinterpret_cast<const float4*>(sd + 3 * kSlots + 8 * i + 4 * half);
+        dIl[i][0] = u.x;
+        dIl[i][1] = u.y;
+        dIl[i][2] = u.z;
+        dIl[i][3] = u.w;
+      }
     }
-    uint32_t gp[4][2];
+    uint32_t gp[4][2], gl[4][2];
     uint32_t maskword = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float gv[4];
+      float gv[4], lv[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const float sv = s_cur[4 * i + rr];
         const bool pos = sv > 0.f;
         gv[rr] = pos ? dIv[i][rr] : 0.f;
+        if (SPLIT) lv[rr] = pos ? dIl[i][rr] : 0.f;
         dw_acc = fmaf(gv[rr], sv, dw_acc);
         // low half of the ballot: slot 8*i + rr, high half: slot 8*i + 4 + rr;
         // lane j of maskword takes the sign word of slot j
@@ -457,6 +472,10 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
       gp[i][0] = pack_bf16(gv[0], gv[1]);
       gp[i][1] = pack_bf16(gv[2], gv[3]);
+      if (SPLIT) {
+        gl[i][0] = pack_bf16(lv[0], lv[1]);
+        gl[i][1] = pack_bf16(lv[2], lv[3]);
+      }
     }
     if (NG == 2 && g == 1 && lane < kSlots) w1x[(c & 1) * kSlots + lane] = maskword;
 
@@ -467,11 +486,14 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4_t aop = u32x4_t{gp[2 * ks][0], gp[2 * ks][1], gp[2 * ks + 1][0], gp[2 * ks + 1][1]};
+      const u32x4_t alo = u32x4_t{gl[2 * ks][0], gl[2 * ks][1], gl[2 * ks + 1][0], gl[2 * ks + 1][1]};
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
         const int col0 = 32 * nd + 16 * ((lane >> 4) & 1);
         const int r0 = 16 * ks + 4 * half;
-        dqacc[nd] = mfma32(aop, L::tr8(ktile(c), r0, r0 + 8, col0), dqacc[nd]);
+        const u32x4_t kt = L::tr8(ktile(c), r0, r0 + 8, col0);
+        dqacc[nd] = mfma32(aop, kt, dqacc[nd]);
+        if (SPLIT) dqacc[nd] = mfma32(alo, kt, dqacc[nd]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -526,10 +548,19 @@ hipError_t launch_t(const Problem& P, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   stage_done(0, "row_prep_kernel");
-  if (P.HP > 32)
-    row_export_kernel<D, DENSE, 2><<<grid, 128, ExportLds<D>::kBytes, stream>>>(P);
-  else
-    row_export_kernel<D, DENSE, 1><<<grid, 64, ExportLds<D>::kBytes, stream>>>(P);
+  // bf16 outputs take G' in two bf16 terms (the dQ rounding then stays the
+  // only one of note); fp32 outputs keep one
+  if (P.HP > 32) {
+    if (P.bf16_out)
+      row_export_kernel<D, DENSE, 2, true><<<grid, 128, ExportLds<D>::kBytes, stream>>>(P);
+    else
+      row_export_kernel<D, DENSE, 2, false><<<grid, 128, ExportLds<D>::kBytes, stream>>>(P);
+  } else {
+    if (P.bf16_out)
+      row_export_kernel<D, DENSE, 1, true><<<grid, 64, ExportLds<D>::kBytes, stream>>>(P);
+    else
+      row_export_kernel<D, DENSE, 1, false><<<grid, 64, ExportLds<D>::kBytes, stream>>>(P);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   stage_done(1, "row_export_kernel");
   return hipSuccess;

@@ -76,7 +76,8 @@ extern "C" {
 
 /* Status codes. */
 #define IBWD_OK 0
-#define IBWD_ERR_INVALID_ARGUMENT -1 /* null pointer, bad shape, misaligned, workspace too small */
+#define IBWD_ERR_INVALID_ARGUMENT -1 /* null pointer, bad shape (topk > S_k included), misaligned,
+                                        workspace too small */
 #define IBWD_ERR_UNSUPPORTED_DEVICE -2 /* the current device is not gfx950 */
 #define IBWD_ERR_HIP -3              /* a HIP runtime call or launch failed */
 
@@ -87,16 +88,20 @@ extern "C" {
                                       d_k not bitwise reproducible */
 #define IBWD_FLAG_GLOBAL_IDS 4u    /* indexer_bwd_sparse only: topk_ids index the flattened
                                       [B*S_k] key array instead of the batch's own keys */
-#define IBWD_FLAG_BF16_OUT 8u      /* d_q, d_w and d_k are bf16 arrays: each element is the
-                                      fp32 result of the same call without this flag, rounded
-                                      to nearest even (PR #730 harness: bf16 dQ and dW, dK cast
-                                      to bf16).  Default route only; not with
+#define IBWD_FLAG_BF16_OUT 8u      /* d_q, d_w and d_k are bf16 arrays (PR #730 harness: bf16
+                                      dQ and dW, dK cast to bf16), each rounded to nearest
+                                      even from fp32: d_w and d_k from the fp32 results of the
+                                      same call without this flag, d_q from a dQ whose G enters
+                                      its product as two bf16 terms (bf16(G) and the bf16 of
+                                      the remainder), so that the output rounding is its only
+                                      error of note.  Default route only; not with
                                       IBWD_FLAG_ATOMIC_DK, whose dK accumulates in d_k */
 
 /*
  * indexer_bwd_sparse — backward of the top-k (sparse) indexer.
  *
- *   topk_ids     [B,S_q,topk] int32, batch-local key ids (see padding above).
+ *   topk_ids     [B,S_q,topk] int32, batch-local key ids (see padding above);
+ *                1 <= topk <= S_k (a larger topk is IBWD_ERR_INVALID_ARGUMENT).
  *                With IBWD_FLAG_GLOBAL_IDS the ids are global instead (the
  *                factory flag topk_indices_global of PR #730's benchmark
  *                harness): a row of batch b selects key id - b*S_k of its own

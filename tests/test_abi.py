@@ -40,6 +40,7 @@ def test_strerror_and_workspace():
     assert ibwd.indexer_bwd_workspace_bytes(True, 2, 64, 64, 4, 32, 0, 0) >= 2 * 64 * 64 * 16
     assert ibwd.indexer_bwd_workspace_bytes(False, 0, 1, 1, 1, 32, 1, 0) == 0
     assert ibwd.indexer_bwd_workspace_bytes(False, 1, 1, 1, 1, 48, 1, 0) == 0
+    assert ibwd.indexer_bwd_workspace_bytes(False, 1, 64, 128, 4, 32, 129, 0) == 0   # topk > S_k
 
 
 # fake, 256-byte aligned "device" addresses: every case below must be rejected
@@ -66,7 +67,7 @@ def call_sparse(a):
     dict(q=None), dict(k=None), dict(w=None), dict(ids=None), dict(I=None), dict(p=None),
     dict(dq=None), dict(dw=None), dict(dk=None),
     dict(B=0), dict(S_q=0), dict(S_k=-1), dict(H=0), dict(H=65), dict(D=48), dict(D=256),
-    dict(topk=0), dict(flags=3), dict(flags=7), dict(flags=10), dict(flags=16), dict(q=A + 8), dict(dk=A + 0x800004),
+    dict(topk=0), dict(topk=129), dict(topk=129, flags=2, ws=None, ws_bytes=0), dict(flags=3), dict(flags=7), dict(flags=10), dict(flags=16), dict(q=A + 8), dict(dk=A + 0x800004),
     dict(w=A + 0x200002), dict(ws=None, ws_bytes=0), dict(ws=A + 0x900000, ws_bytes=16),
     dict(ws=A + 0x900010, ws_bytes=1 << 30), dict(flags=1, ws=None, ws_bytes=1 << 30),
     dict(B=1 << 20, S_q=1 << 20, H=64, D=128), dict(S_k=1024 * 256 + 1, D=128, ws_bytes=1 << 40),
@@ -160,3 +161,41 @@ def test_forward_and_topk_without_gpu_fail_cleanly():
                                   0, None) in (ibwd.IBWD_ERR_HIP, ibwd.IBWD_ERR_UNSUPPORTED_DEVICE)
     assert lib.indexer_topk(A, A + 0x400000, None, 8, 64, 16, None) in (
         ibwd.IBWD_ERR_HIP, ibwd.IBWD_ERR_UNSUPPORTED_DEVICE)
+
+
+def test_binding_allocates_the_workspace_on_the_launch_stream(monkeypatch):
+    """A workspace the binding allocates belongs to the stream the kernels run
+    on (it is released when the call returns; the caching allocator may then
+    reuse it only in that stream's order)."""
+    torch = pytest.importorskip("torch")
+    import contextlib
+
+    entered = []
+
+    @contextlib.contextmanager
+    def fake_stream(s):
+        entered.append(s)
+        try:
+            yield
+        finally:
+            entered.pop()
+
+    made = []
+    real_empty = torch.empty
+
+    def fake_empty(*a, **kw):
+        made.append(entered[-1] if entered else None)
+        kw["device"] = "cpu"
+        return real_empty(*a, **kw)
+
+    monkeypatch.setattr(torch.cuda, "stream", fake_stream)
+    monkeypatch.setattr(torch, "empty", fake_empty)
+    side = object()
+    ws, nbytes = ibwd._workspace(False, 1, 64, 128, 4, 32, 16, 0, None, "cpu", side)
+    assert made == [side]
+    assert nbytes == ibwd.indexer_bwd_workspace_bytes(False, 1, 64, 128, 4, 32, 16, 0) > 0
+    # a caller's workspace is used as given; the atomic route needs none
+    assert ibwd._workspace(False, 1, 64, 128, 4, 32, 16, 0, ws, "cpu", side)[0] is ws
+    assert ibwd._workspace(False, 1, 64, 128, 4, 32, 16, ibwd.IBWD_FLAG_ATOMIC_DK, None, "cpu",
+                           side) == (None, 0)
+    assert made == [side]

@@ -22,9 +22,7 @@ pytestmark = pytest.mark.gpu
 DQ_DW_REL = 2e-3
 DQ_DW_MAXABS = 1e-2
 DK_REL = 5e-3
-# bf16 outputs: rounding to nearest changes each value by at most its unit
-# roundoff 2^-8 (8 significant bits), so ||bf16 - ref|| <= ||fp32 - ref|| +
-# 2^-8 ||fp32||: each bar grows by 2^-8 (times 1 + bar for ||fp32|| / ||ref||)
+# unit roundoff of bf16 (8 significant bits)
 BF16_U = 2.0 ** -8
 
 
@@ -76,9 +74,8 @@ def run(ibwd, x, t=None, deterministic=False, atomic_dk=False, bf16_out=False):
     return host(r)
 
 
-def assert_parity(name, got, ref, round_u=0.0):
-    """The bars above; round_u > 0 widens each by an output rounding of that
-    unit roundoff (bf16 outputs)."""
+def assert_parity(name, got, ref):
+    """The bars above, for fp32 and bf16 outputs alike."""
     dq, dw, dk = got
     rq, rw, rk = ref
     e = dict(dq=relrms(dq, rq), dw=relrms(dw, rw), dk=relrms(dk, rk),
@@ -88,11 +85,9 @@ def assert_parity(name, got, ref, round_u=0.0):
     for a in (dq, dw, dk):
         assert np.isfinite(a).all()
 
-    def bar(b):
-        return b + round_u * (1.0 + b)
-    assert e["dq"] <= bar(DQ_DW_REL) and e["dq_max"] <= bar(DQ_DW_MAXABS), e
-    assert e["dw"] <= bar(DQ_DW_REL) and e["dw_max"] <= bar(DQ_DW_MAXABS), e
-    assert e["dk"] <= bar(DK_REL), e
+    assert e["dq"] <= DQ_DW_REL and e["dq_max"] <= DQ_DW_MAXABS, e
+    assert e["dw"] <= DQ_DW_REL and e["dw_max"] <= DQ_DW_MAXABS, e
+    assert e["dk"] <= DK_REL, e
     return e
 
 
@@ -213,18 +208,28 @@ def test_global_ids(ibwd, atomic_dk):
 
 @pytest.mark.parametrize("name,S_q", [("tiny", 64), ("anchor", 192), ("dense", 160)])
 def test_bf16_outputs(ibwd, name, S_q):
-    """bf16 outputs are the fp32 outputs of the same call rounded to nearest
-    even, bit for bit, and within the widened bars of the oracle."""
+    """bf16 outputs within the same bars as fp32 outputs (not widened): d_w and
+    d_k are the fp32 outputs of the same call rounded to nearest even, bit for
+    bit; d_q is rounded from a dQ whose G' enters GEMM2 as two bf16 terms."""
     log(f"case: bf16 outputs {name} S_q={S_q}")
     x = make_inputs(name, S_q=S_q, seed=51)
     t = dev_inputs(x)
     f32 = run(ibwd, x, t)
     b16 = run(ibwd, x, t, bf16_out=True)
-    for a, b in zip(f32, b16):
-        assert b.dtype == np.uint16
-        assert np.array_equal(b, bf16_rne_bits(a))
-    assert_parity(f"bf16-{name}", [bf16_bits_to_f32(b) for b in b16],
-                  oracle.Problem.from_inputs(x).backward(), round_u=BF16_U)
+    for a in b16:
+        assert a.dtype == np.uint16
+    assert np.array_equal(b16[1], bf16_rne_bits(f32[1]))
+    assert np.array_equal(b16[2], bf16_rne_bits(f32[2]))
+    ref = oracle.Problem.from_inputs(x).backward()
+    e = assert_parity(f"bf16-{name}", [bf16_bits_to_f32(b) for b in b16], ref)
+    # every d_q element is the oracle's value up to one rounding to bf16 (half a
+    # unit in the last place, 2^-8 relative) and fp32 accumulation error: the
+    # G' of its product lost nothing to bf16
+    dq = bf16_bits_to_f32(b16[0]).astype(np.float64)
+    rq = ref[0]
+    slack = 1e-5 * np.abs(rq).max()
+    assert np.all(np.abs(dq - rq) <= BF16_U * np.abs(rq) + slack), np.max(
+        np.abs(dq - rq) - BF16_U * np.abs(rq))
 
 
 @pytest.mark.parametrize("bf16_out", [False, True])
@@ -385,27 +390,53 @@ def test_invalid_call_leaves_outputs_untouched(ibwd):
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads, in the configuration the benchmark times: every output
-# compared (the oracle takes seconds on the host cores)
+# full-size workloads, in the configuration the benchmark times: every element
+# of d_q, d_w and d_k against the full oracle backward (seconds on the host
+# cores)
 
 @pytest.mark.parametrize("name", ["sparse", "anchor", "wide", "dense"])
 def test_full_size_workload(ibwd, name):
     log(f"case: full-size {name}")
     x = make_inputs(name, device="cuda:0")
     got = run(ibwd, x)
-    prob = oracle.Problem.from_inputs(x)
-    rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(x.wl.S_q, size=64, replace=False))
-    keys = np.sort(rng.choice(x.wl.S_k, size=48, replace=False))
-    rq, rw = prob.rows(rows)
-    rk = prob.dk_rows(keys)
-    e = assert_parity(f"full-{name} (sampled rows/keys)", (got[0][0, rows], got[1][0, rows], got[2][0, keys]),
-                      (rq, rw, rk))
+    ref = oracle.Problem.from_inputs(x).backward()
+    assert_parity(f"full-{name}", got, ref)
     # Euler identity of the 1-homogeneous score at every (t,h): <q, dQ> = w dW
     q = oracle.widen_bf16(x.q)
     lhs = np.einsum("bthd,bthd->bth", q, got[0].astype(np.float64))
     rhs = x.w.astype(np.float64) * got[1].astype(np.float64)
-    assert relrms(lhs, rhs) < 2e-2, relrms(lhs, rhs)
+    e = relrms(lhs, rhs)
+    log(f"full-{name}: euler relRMS {e:.3e}")
+    assert e < 6e-3, e
+
+
+@pytest.mark.parametrize("topk", [128, 256, 384, 640, 1536])
+def test_topk_sweep_anchor_shapes(ibwd, topk):
+    """The topk sweep points at the anchor's H, D and S_k (256 queries, 2%
+    padding): every element against the oracle."""
+    log(f"case: topk sweep {topk}")
+    wl = dataclasses.replace(WORKLOADS["anchor"], S_q=256, topk=topk)
+    x = make_inputs(wl, seed=300 + topk)
+    assert_parity(f"topk-{topk}", run(ibwd, x), oracle.Problem.from_inputs(x).backward())
+
+
+def test_side_stream_without_workspace(ibwd):
+    """A call on a side stream with no workspace, followed at once by
+    allocations and fills on the current stream: the workspace the binding
+    allocates belongs to the side stream, so that work cannot take its memory
+    while the kernels run.  The outputs equal those of a plain call."""
+    log("case: side stream, binding-allocated workspace")
+    x = make_inputs("anchor", S_q=512, seed=71)
+    t = dev_inputs(x)
+    ref = run(ibwd, x, t)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    r = call(ibwd, x, t, stream=s)
+    junk = [torch.full((1 << 22,), float(i), device="cuda:0") for i in range(16)]
+    torch.cuda.synchronize()
+    for u, v in zip(host(r), ref):
+        assert np.array_equal(u, v)
+    del junk
 
 
 def test_stage_hook_reports_every_kernel(ibwd):
