@@ -14,6 +14,8 @@ from typing import Optional, Tuple
 
 __all__ = [
     "indexer_bwd_sparse",
+    "indexer_bwd_sparse_noalloc",
+    "IBWD_NOALLOC_SCRATCH_BYTES",
     "indexer_bwd_dense",
     "indexer_fwd_scores",
     "indexer_topk",
@@ -40,6 +42,7 @@ IBWD_FLAG_DETERMINISTIC = 1
 IBWD_FLAG_ATOMIC_DK = 2
 IBWD_FLAG_GLOBAL_IDS = 4
 IBWD_FLAG_BF16_OUT = 8
+IBWD_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_indexer_bwd.so")
 _lib = None
@@ -66,6 +69,9 @@ def library() -> ctypes.CDLL:
         lib.indexer_bwd_sparse.argtypes = [vp] * 9 + [i64] * 6 + [f32, f32, ctypes.c_uint32, vp,
                                                                   ctypes.c_size_t, vp]
         lib.indexer_bwd_sparse.restype = ctypes.c_int
+        lib.indexer_bwd_sparse_noalloc.argtypes = [vp] * 9 + [i64] * 6 + [f32, f32,
+                                                                          ctypes.c_uint32, vp]
+        lib.indexer_bwd_sparse_noalloc.restype = ctypes.c_int
         lib.indexer_bwd_dense.argtypes = [vp] * 8 + [i64] * 6 + [f32, f32, ctypes.c_uint32, vp,
                                                                  ctypes.c_size_t, vp]
         lib.indexer_bwd_dense.restype = ctypes.c_int
@@ -201,6 +207,40 @@ def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w
         _ptr(q), _ptr(k), _ptr(w), _ptr(topk_ids), _ptr(index_score), _ptr(attn_score), _ptr(d_q),
         _ptr(d_w), _ptr(d_k), B, S_q, S_k, H, D, topk, float(sm_scale), float(grad_loss), flags,
         _ptr(workspace), ws_bytes, int(s.cuda_stream))
+    if st != IBWD_OK:
+        raise IndexerBwdError(st)
+    return d_q, d_w, d_k
+
+
+def indexer_bwd_sparse_noalloc(q, k, w, topk_ids, index_score, attn_score, d_q, d_w, d_k, *,
+                               sm_scale: float = 1.0, grad_loss: float = 1.0,
+                               deterministic: bool = False, atomic_dk: bool = False,
+                               global_ids: bool = False, bf16_out: bool = False, stream=None):
+    """indexer_bwd_sparse through the allocation-free entry point: the library's
+    own per-GPU scratch array (IBWD_NOALLOC_SCRATCH_BYTES) instead of a workspace.
+    The outputs must be given (nothing is allocated here); returns them."""
+    torch = _torch()
+    if d_q is None or d_w is None or d_k is None:
+        raise ValueError("indexer_bwd_sparse_noalloc allocates nothing: pass d_q, d_w and d_k")
+    B, S_q, H, D = q.shape
+    S_k = k.shape[1]
+    topk = topk_ids.shape[-1]
+    _check(q, torch.bfloat16, (B, S_q, H, D), "q")
+    _check(k, torch.bfloat16, (B, S_k, D), "k")
+    _check(w, torch.float32, (B, S_q, H), "w")
+    _check(topk_ids, torch.int32, (B, S_q, topk), "topk_ids")
+    _check(index_score, torch.float32, (B, S_q, topk), "index_score")
+    _check(attn_score, torch.float32, (B, S_q, topk), "attn_score")
+    dt = torch.bfloat16 if bf16_out else torch.float32
+    for t, shp, name in zip((d_q, d_w, d_k), ((B, S_q, H, D), (B, S_q, H), (B, S_k, D)),
+                            ("d_q", "d_w", "d_k")):
+        _check(t, dt, shp, name)
+    flags = _flags(deterministic, atomic_dk, bf16_out) | (IBWD_FLAG_GLOBAL_IDS if global_ids else 0)
+    s = _stream(stream, q.device)
+    st = library().indexer_bwd_sparse_noalloc(
+        _ptr(q), _ptr(k), _ptr(w), _ptr(topk_ids), _ptr(index_score), _ptr(attn_score), _ptr(d_q),
+        _ptr(d_w), _ptr(d_k), B, S_q, S_k, H, D, topk, float(sm_scale), float(grad_loss), flags,
+        int(s.cuda_stream))
     if st != IBWD_OK:
         raise IndexerBwdError(st)
     return d_q, d_w, d_k

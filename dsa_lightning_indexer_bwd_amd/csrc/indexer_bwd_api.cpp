@@ -11,6 +11,9 @@
 #include "fwd_launch.h"
 #include "launch.h"
 
+static_assert(IBWD_NOALLOC_SCRATCH_BYTES == ibwd::kNoAllocScratchBytes,
+              "the header states the scratch size of the allocation-free entry point");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -74,25 +77,27 @@ size_t workspace_bytes(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D
   return ibwd::make_layout(B, S_q, S_k, H, D, row_len).total;
 }
 
-}  // namespace
-
-extern "C" {
-
-int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32_t* topk_ids,
-                       const float* index_score, const float* attn_score, void* d_q, void* d_w,
-                       void* d_k, int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
-                       int64_t topk, float sm_scale, float grad_loss, uint32_t flags,
-                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+// Both sparse entry points: every check first, then the launch.  noalloc: the
+// scratch is the library's per-device array (no workspace argument).
+int sparse_call(const void* q, const void* k, const float* w, const int32_t* topk_ids,
+                const float* index_score, const float* attn_score, void* d_q, void* d_w, void* d_k,
+                int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D, int64_t topk,
+                float sm_scale, float grad_loss, uint32_t flags, void* workspace, size_t ws_bytes,
+                hipStream_t stream, bool noalloc) {
   int st = check_common(q, k, w, index_score, attn_score, d_q, d_w, d_k, B, S_q, S_k, H, D, topk,
                         flags);
   if (st != IBWD_OK) return st;
   if (!topk_ids || !aligned(topk_ids, 4)) return IBWD_ERR_INVALID_ARGUMENT;
   if (topk > S_k) return IBWD_ERR_INVALID_ARGUMENT;  // more slots than keys
-  size_t need = workspace_bytes(B, S_q, S_k, H, D, topk, flags);
-  if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256)))
+  const size_t need = workspace_bytes(B, S_q, S_k, H, D, topk, flags);
+  if (noalloc) {
+    if (need > ibwd::kNoAllocScratchBytes) return IBWD_ERR_INVALID_ARGUMENT;
+  } else if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256))) {
     return IBWD_ERR_INVALID_ARGUMENT;
+  }
   st = device_status();
   if (st != IBWD_OK) return st;
+  if (noalloc && need > 0 && ibwd::noalloc_scratch(&workspace) != hipSuccess) return IBWD_ERR_HIP;
   ibwd::Problem P{};
   P.q = static_cast<const uint16_t*>(q);
   P.k = static_cast<const uint16_t*>(k);
@@ -118,6 +123,29 @@ int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32
   P.grad_loss = grad_loss;
   P.route = (flags & IBWD_FLAG_ATOMIC_DK) ? ibwd::kDkAtomic : ibwd::kDkTwoPass;
   return ibwd::launch(P, workspace, stream) == hipSuccess ? IBWD_OK : IBWD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32_t* topk_ids,
+                       const float* index_score, const float* attn_score, void* d_q, void* d_w,
+                       void* d_k, int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
+                       int64_t topk, float sm_scale, float grad_loss, uint32_t flags,
+                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return sparse_call(q, k, w, topk_ids, index_score, attn_score, d_q, d_w, d_k, B, S_q, S_k, H, D,
+                     topk, sm_scale, grad_loss, flags, workspace, ws_bytes, stream, false);
+}
+
+int indexer_bwd_sparse_noalloc(const void* q, const void* k, const float* w,
+                               const int32_t* topk_ids, const float* index_score,
+                               const float* attn_score, void* d_q, void* d_w, void* d_k, int64_t B,
+                               int64_t S_q, int64_t S_k, int64_t H, int64_t D, int64_t topk,
+                               float sm_scale, float grad_loss, uint32_t flags,
+                               hipStream_t stream) {
+  return sparse_call(q, k, w, topk_ids, index_score, attn_score, d_q, d_w, d_k, B, S_q, S_k, H, D,
+                     topk, sm_scale, grad_loss, flags, nullptr, 0, stream, true);
 }
 
 int indexer_bwd_dense(const void* q, const void* k, const float* w, const float* index_score,

@@ -12,10 +12,41 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "launch.h"
 
+namespace {
+
+// Scratch of the allocation-free entry point: one array per GPU, held until
+// the process ends.  Host code never passes `scratch` itself to a kernel (in
+// host code it names a host-side stand-in); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[ibwd::kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+
+}  // namespace
+
 namespace ibwd {
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    // with device `dev` current: its copy of the array
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 __global__ void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {

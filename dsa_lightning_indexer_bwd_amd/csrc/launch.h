@@ -117,6 +117,11 @@ void stage_done(int stage, const char* kernel);
 // Enqueue the whole backward on `stream`.  Returns the first HIP error.
 hipError_t launch(Problem P, void* workspace, hipStream_t stream);
 
+// Size of the library-owned scratch array of the allocation-free entry point,
+// and its device address on the current device (resolved once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Row kernel of the atomic route (one wave per query row): dQ, dW and the fp32
 // atomic dK scatter.
 hipError_t launch_rows(const Problem& P, hipStream_t stream);

@@ -130,6 +130,34 @@ int indexer_bwd_sparse(const void* q, const void* k, const float* w, const int32
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * indexer_bwd_sparse_noalloc — indexer_bwd_sparse for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no workspace; its scratch is a
+ * library-owned device array of IBWD_NOALLOC_SCRATCH_BYTES bytes (a
+ * file-scope device variable: each GPU the library runs on holds its own copy
+ * until the process ends).  The call allocates and frees nothing; the first
+ * call on a device resolves the array's address on that device (make one
+ * before capturing a graph).  The caller passes inputs and outputs exactly as
+ * for indexer_bwd_sparse.
+ *   - A call whose indexer_bwd_workspace_bytes(0, B, S_q, S_k, H, D, topk,
+ *     flags) exceeds IBWD_NOALLOC_SCRATCH_BYTES returns
+ *     IBWD_ERR_INVALID_ARGUMENT before anything is written or launched (at
+ *     H=64, D=128, S_k=4096, topk=1024 the limit is 2354 query rows).
+ *   - Every call on a GPU shares that GPU's array, which keeps the last call's
+ *     contents; no part of it needs clearing (each location a kernel reads is
+ *     written earlier in the same call).  Calls that overlap on one GPU (other
+ *     streams, other threads) race on the array: the caller must order them.
+ * Arguments, flags, results and other errors as for indexer_bwd_sparse.
+ */
+#define IBWD_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int indexer_bwd_sparse_noalloc(const void* q, const void* k, const float* w,
+                               const int32_t* topk_ids, const float* index_score,
+                               const float* attn_score, void* d_q, void* d_w, void* d_k, int64_t B,
+                               int64_t S_q, int64_t S_k, int64_t H, int64_t D, int64_t topk,
+                               float sm_scale, float grad_loss, uint32_t flags,
+                               hipStream_t stream);
+
+/*
  * indexer_bwd_dense — backward of the dense causal indexer: query t of a batch
  * selects every key s with 0 <= s <= t + q_offset (and s < S_k); a row with no
  * such key contributes nothing (PR #549 names a separate dense indexer-backward
