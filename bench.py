@@ -44,8 +44,8 @@ def parse():
                     help="time the step before the backward instead: indexer scores over every "
                          "key plus the top-k selection, at the workload's shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="target wall time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=18.0,
+                    help="target wall time of the oracle sample (three timed runs)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a kernel of "
                          "known traffic, read by the HBM counter runs to scale them)")
@@ -125,6 +125,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    clk_before = read_gfx_clock()
+    print("bench: clock under load", file=sys.stderr, flush=True)
+    clk_load = clocks_under_load(step, torch.cuda.synchronize)
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
     # HIP events recorded on the stream the kernels run on: one pair around
     # every call, and one after every kernel of the call (the library's stage
@@ -150,6 +153,7 @@ def main():
         e1.record(stream)
     t_all1.record(stream)
     torch.cuda.synchronize()
+    clk_after = read_gfx_clock()
     ibwd.set_stage_hook(None)
     per_call_ms = [e0.elapsed_time(e1) for e0, e1 in calls]
     total_ms = t_all0.elapsed_time(t_all1)
@@ -227,6 +231,7 @@ def main():
             "algorithmic_work": dom["algorithmic_work"],
         },
         "kernels": kernels,
+        "clocks": clock_report(clk_before, clk_load, clk_after, tflops, dom),
         "call_hbm_algorithmic_bytes": hbm_bytes,
         "pages_context": {"kernel_gemm_us_B200_anchor": 1688.8,
                           "note": "NVIDIA B200 figure from the pages; context only"},
@@ -388,6 +393,79 @@ def cpu_baseline_forward(x, wl, topk, causal, flops, seconds):
             "us_per_call_extrapolated": round(full_s * 1e6, 1)}
 
 
+def clock_report(before, load, after, tflops, dom):
+    """amd-smi GFX clocks around the timed region, and the bf16 peak rescaled
+    from its 2.4 GHz rating to the clock measured under load."""
+    rep = {"before_timing": before, "under_load": load, "after_timing": after,
+           "source": "amd-smi metric -c (mean of the accelerator dies' GFX clocks)"}
+    if load and load.get("mhz"):
+        peak = PEAK_BF16_TFLOPS * load["mhz"] / 2400.0
+        rep["bf16_peak_at_load_clock_tflops"] = round(peak, 1)
+        rep["frac_of_bf16_peak_at_load_clock"] = round(tflops / peak, 4)
+        if dom["unit"] == "TFLOP/s":
+            rep["roofline_frac_at_load_clock"] = round(dom["achieved"] / peak, 4)
+    return rep
+
+
+def read_gfx_clock():
+    """GFX clock of the GPU as amd-smi reports it now: {"mhz": mean over the
+    accelerator dies' current clocks, "max_mhz": their rated maximum}, or None
+    when amd-smi is unavailable.  The clocks drop to a few hundred MHz when the
+    GPU idles, so a sample means something only while kernels run."""
+    import subprocess
+
+    try:
+        res = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
+                             timeout=20)
+        start = res.stdout.find("{")
+        data = json.loads(res.stdout[start:]) if start >= 0 else None
+        gpus = data["gpu_data"] if isinstance(data, dict) else data
+        clocks = gpus[0]["clock"]
+        cur = [v["clk"]["value"] for key, v in clocks.items()
+               if key.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        mx = [v["max_clk"]["value"] for key, v in clocks.items()
+              if key.startswith("gfx_") and isinstance(v.get("max_clk"), dict)]
+        cur = [float(c) for c in cur if isinstance(c, (int, float))]
+        mx = [float(c) for c in mx if isinstance(c, (int, float))]
+        if not cur:
+            return None
+        return {"mhz": round(sum(cur) / len(cur), 1), "max_mhz": max(mx) if mx else None}
+    except Exception:
+        return None
+
+
+def clocks_under_load(step, sync, samples=3, spacing=1.0):
+    """GFX clock under load: amd-smi sampled `samples` times, `spacing` seconds
+    apart after a first second of load, from a thread while the main thread
+    keeps running calls (untimed).  The driver's clock figures are refreshed
+    about once a second, so samples of a shorter run repeat one stale value.
+    Returns {"mhz": mean of the samples, "samples_mhz": [...], "max_mhz": ...}."""
+    import threading
+
+    got = []
+
+    def sample():
+        for _ in range(samples):
+            time.sleep(spacing)
+            got.append(read_gfx_clock())
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() and time.perf_counter() - t0 < samples * spacing + 30.0:
+        for _ in range(8):
+            step()
+        sync()
+    th.join(timeout=30.0)
+    sync()
+    vals = [g for g in got if g]
+    if not vals:
+        return None
+    mhz = [g["mhz"] for g in vals]
+    return {"mhz": round(sum(mhz) / len(mhz), 1), "samples_mhz": mhz,
+            "max_mhz": vals[0].get("max_mhz")}
+
+
 def kernel_model(name, wl, B, H, D, S_q, S_k, out_bytes=4):
     """(bound, algorithmic work per launch) of one kernel of the call.
 
@@ -469,12 +547,16 @@ def cpu_baseline(x, wl, target_s):
     t0 = time.perf_counter()
     oracle.Problem.from_inputs(sub(n0)).backward()
     t_cal = time.perf_counter() - t0
-    n = int(min(wl.S_q, max(n0, n0 * target_s / max(t_cal, 1e-3))))
+    # three timed runs of about target_s / 3 each; the median is reported
+    n = int(min(wl.S_q, max(n0, n0 * target_s / 3.0 / max(t_cal, 1e-3))))
     xs = sub(n)
     prob = oracle.Problem.from_inputs(xs)
-    t0 = time.perf_counter()
-    prob.backward()
-    dt = time.perf_counter() - t0
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        prob.backward()
+        runs.append(time.perf_counter() - t0)
+    dt = statistics.median(runs)
     fl = xs.wl.flops()
     return {
         "value": round(fl / dt / 1e12, 6),
@@ -482,7 +564,9 @@ def cpu_baseline(x, wl, target_s):
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": "first %d of %d query rows of the %s workload (full backward of those rows incl. "
-                  "their dK scatter), %.2f s wall" % (n, wl.S_q, wl.name, dt),
+                  "their dK scatter); median of 3 runs: %s s wall"
+                  % (n, wl.S_q, wl.name, ", ".join("%.2f" % r for r in runs)),
+        "runs_s": [round(r, 3) for r in runs],
         "us_per_call_extrapolated": round(dt * wl.S_q / n * 1e6, 1),
         "nproc": os.cpu_count(),
     }
