@@ -8,6 +8,7 @@ is no fallback.  If the library is not built this module raises on first use.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -45,6 +46,7 @@ IBWD_FLAG_BF16_OUT = 8
 IBWD_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_indexer_bwd.so")
+DEEPBUF_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_indexer_bwd_deepbuf.so")
 _lib = None
 _HOOK_T = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p)
 _hook_ref = None  # keeps the ctypes callback alive while it is installed
@@ -56,13 +58,36 @@ class IndexerBwdError(RuntimeError):
         super().__init__("indexer_bwd failed (%d): %s" % (status, indexer_bwd_strerror(status)))
 
 
+_loaded = {}  # path -> handle of every build loaded in this process
+
+
 def library() -> ctypes.CDLL:
     """The loaded C library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError("HIP library %s is missing: run __graft_entry__.build() first" % LIB_PATH)
-        lib = ctypes.CDLL(LIB_PATH)
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route this module's calls to another build of the library while the
+    block runs (a verification aid: the build with deeper buffer rings,
+    DEEPBUF_LIB_PATH, must give the same bits as the library)."""
+    global _lib
+    prev = library()
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if path not in _loaded:
+        if not os.path.exists(path):
+            raise RuntimeError("HIP library %s is missing: run __graft_entry__.build() first" % path)
+        lib = ctypes.CDLL(path)
         vp = ctypes.c_void_p
         i64 = ctypes.c_int64
         f32 = ctypes.c_float
@@ -85,8 +110,8 @@ def library() -> ctypes.CDLL:
         lib.indexer_bwd_strerror.restype = ctypes.c_char_p
         lib.indexer_bwd_set_stage_hook.argtypes = [_HOOK_T, ctypes.c_void_p]
         lib.indexer_bwd_set_stage_hook.restype = ctypes.c_int
-        _lib = lib
-    return _lib
+        _loaded[path] = lib
+    return _loaded[path]
 
 
 def set_stage_hook(fn) -> None:

@@ -8,6 +8,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libdsa_indexer_bwd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# A second build whose kernels keep deeper buffer rings (IBWD_DEEP_BUFFERS) with
+# the same copy schedule: a verification aid, its results must equal the
+# library's bit for bit (no buffer of the library may be reused too early).
+DEEPBUF_LIB_PATH = os.path.join(PKG, "libdsa_indexer_bwd_deepbuf.so")
+DEEPBUF_SOURCES = ("indexer_bwd_rows_export.hip", "indexer_bwd_dk.hip")
 
 HIP_SOURCES = ["indexer_bwd_kernels.hip", "indexer_bwd_rows.hip", "indexer_bwd_rows_export.hip",
                "indexer_bwd_dk.hip", "indexer_fwd.hip"]
@@ -43,10 +48,23 @@ def build(verbose: bool = False) -> str:
         cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
         _run(cmd, verbose)
         objs.append(obj)
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    _run([hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB_PATH)
+    _link(objs, LIB_PATH, verbose)
+    deep = []
+    for obj in objs:
+        src = os.path.basename(obj)[:-2]
+        if src in DEEPBUF_SOURCES:
+            obj = os.path.join(objdir, src + ".deepbuf.o")
+            _run([hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj, "-DIBWD_DEEP_BUFFERS"]
+                 + COMMON + DEVICE_FLAGS + PER_FILE_FLAGS.get(src, []), verbose)
+        deep.append(obj)
+    _link(deep, DEEPBUF_LIB_PATH, verbose)
     return LIB_PATH
+
+
+def _link(objs, path, verbose):
+    tmp = path + ".tmp%d" % os.getpid()
+    _run([hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs, verbose)
+    os.replace(tmp, path)
 
 
 def _run(cmd, verbose):

@@ -54,6 +54,18 @@ namespace {
 
 constexpr int kXcds = 8;  // accelerator dies of the chip, each with its own L2
 
+// Buffers per ring: Q' tiles, key tables, record stages.  The copies are issued
+// a fixed number of queries ahead whatever the depth (Q' two, records three,
+// tables one), so a build with IBWD_DEEP_BUFFERS (deeper rings, no buffer
+// reused within a copy's window, one workgroup per CU) must produce the same
+// bits as this one; the GPU tests compare the two builds.
+#ifdef IBWD_DEEP_BUFFERS
+constexpr int kQTiles = 4, kTables = 4, kStages = 8;
+#else
+constexpr int kQTiles = 3, kTables = 2, kStages = 4;
+#endif
+static_assert(kQTiles >= 3 && kTables >= 2 && kStages >= 4, "rings cover the copy distances");
+
 template <int D, int HP>
 struct DkShape {
   static constexpr int RK = kRangeKeys;        // keys per range (4 blocks of 32)
@@ -68,10 +80,10 @@ struct DkShape {
   static constexpr int kRowBytes = HP * 2;     // one d row of (w*q)^T
   static constexpr int kCpr = kRowBytes / 16;  // 16-byte chunks per row
   static constexpr int kQBytes = D * kRowBytes;
-  static constexpr int kTOff = 3 * kQBytes;    // three Q' tiles, then two key tables
-  static constexpr int kStOff = kTOff + 2 * RK * 16;  // four record stages {kd, w}
+  static constexpr int kTOff = kQTiles * kQBytes;      // Q' tiles, then key tables,
+  static constexpr int kStOff = kTOff + kTables * RK * 16;  // then record stages {kd, w}
   static constexpr int kStBytes = 2 * kRecBlock * 8;
-  static constexpr int kListOff = kStOff + 4 * kStBytes;
+  static constexpr int kListOff = kStOff + kStages * kStBytes;
   static constexpr int kFlagOff = kListOff + kMaxQueryBlock * 16;
   static constexpr int kBytes = kFlagOff + 16;
   static constexpr int kDmaQ = kQBytes / 1024;  // copies of 64 lanes x 16 B per Q' tile
@@ -80,7 +92,7 @@ struct DkShape {
   // (query passes use 0 .. kMaxQueryBlock-1; 16383 marks a never-written entry)
   static_assert(kDmaW * NW * 1024 == kQBytes, "Q' tile splits into whole copies per wave");
   static_assert(kDmaW < 64, "one iteration's copies fit a vmcnt immediate");
-  static_assert(3 * kQBytes >= kMaxQueryBlock * 4, "Q' tiles double as scan scratch");
+  static_assert(kQTiles * kQBytes >= kMaxQueryBlock * 4, "Q' tiles double as scan scratch");
   static_assert(kRecBlock * 8 == 1024, "one DMA moves a record block of one array");
   static_assert(KBW * 32 * NWK == RK, "key blocks cover the range");
 };
@@ -195,7 +207,7 @@ dk_range_kernel(Problem P) {
   const int nq = int((t0 + P.QBS < P.S_q ? t0 + P.QBS : P.S_q) - t0);
 
   // key tables: no entry carries a pass id of this launch yet
-  for (int i = tid; i < 2 * RK; i += NTH)
+  for (int i = tid; i < kTables * RK; i += NTH)
     reinterpret_cast<uint4*>(lds + S::kTOff)[i] = make_uint4(0, 0, 0, 0xffffffffu);
 
   // ---- the block's queries that have records in this range ------------------
@@ -359,9 +371,9 @@ dk_range_kernel(Problem P) {
   };
 
   // ---- query loop ---------------------------------------------------------------
-  // Query qi: Q' tile qi % 3 (copied two queries ahead by the MMA waves),
-  // record stage qi % 4 (copied three queries ahead by the producer), key
-  // table qi % 2 (built by the producer right after the barrier of query
+  // Query qi: Q' tile qi % kQTiles (copied two queries ahead by the MMA
+  // waves), record stage qi % kStages (copied three queries ahead by the
+  // producer), key table qi % kTables (built by the producer right after the barrier of query
   // qi-1, from the staged records).  Every wave issues its copies and no other
   // vector-memory operation in the loop (except the producer's loads of
   // records past a staged block, which the compiler waits for at once), so
@@ -394,7 +406,7 @@ dk_range_kernel(Problem P) {
       // the copy of iteration qi-1 is records(qi+2) if qi+2 < nne; records(qi+1)
       // is in
       wait_prev(qi + 2 < nne);
-      __syncthreads();  // table qi % 2 is complete; query qi-1 is done
+      __syncthreads();  // table qi % kTables is complete; query qi-1 is done
       const int4 e1 = e_n1, e3 = e_n3;
       const int n = uni(e_cur.z) - uni(e_cur.y);
       e_cur = e1;
@@ -407,11 +419,11 @@ dk_range_kernel(Problem P) {
       // the MMA waves wait for this table at the next barrier: the producer's
       // work of the iteration runs at the highest priority of the CU's waves
       __builtin_amdgcn_s_setprio(2);
-      if (qi + 1 < nne) scatter(e1, (qi + 1) & 3, (qi + 1) & 1, qi + 1, key);
-      dup = dup || lost_any(n, kq, qi & 1, qi);
-      // stage (qi+3) % 4 = (qi-1) % 4 was last read by the scatter of query
+      if (qi + 1 < nne) scatter(e1, (qi + 1) % kStages, (qi + 1) % kTables, qi + 1, key);
+      dup = dup || lost_any(n, kq, qi % kTables, qi);
+      // stage (qi+3) % kStages was last read at the latest by the scatter of query
       // qi-1, whose table writes waited for those reads
-      if (qi + 3 < nne) dma_recs(uni(e3.x), uni(e3.y), (qi + 3) & 3);
+      if (qi + 3 < nne) dma_recs(uni(e3.x), uni(e3.y), (qi + 3) % kStages);
       __builtin_amdgcn_s_setprio(0);
     }
   } else {
@@ -426,24 +438,24 @@ dk_range_kernel(Problem P) {
       // the copy of "iteration -1": Q'(1)
       if (nne > 1) dma_qt(list[1].x, 1);
     }
-    int q0 = 0, q2 = 2;  // qi % 3, (qi+2) % 3
+    int q0 = 0, q2 = 2;  // qi % kQTiles, (qi+2) % kQTiles
     int row2 = nne > 2 ? list[2].x : 0;  // read one iteration before it is needed
     for (int qi = 0; qi < nne; ++qi) {
       // the copy of iteration qi-1 is Q'(qi+1) if qi+1 < nne; this wave's
       // share of Q'(qi) is in
       wait_prev(qi + 1 < nne);
-      __syncthreads();  // every share of Q'(qi), and table qi % 2, are complete
-      // Q' tile (qi+2) % 3 was last read in query qi-1
+      __syncthreads();  // every share of Q'(qi), and table qi % kTables, are complete
+      // Q' tile (qi+2) % kQTiles was last read in query qi-1 at the latest
       const int r2 = row2;
       if (qi + 3 < nne) row2 = list[qi + 3].x;
       if (qi + 2 < nne) dma_qt(r2, q2);
       // raised priority while this wave expands and issues its MFMAs, so that
       // the other MMA wave of the SIMD fills the gaps with its own work
       __builtin_amdgcn_s_setprio(1);
-      mfma_pass(qi & 1, q0, qi);
+      mfma_pass(qi % kTables, q0, qi);
       __builtin_amdgcn_s_setprio(0);
-      q0 = q0 == 2 ? 0 : q0 + 1;
-      q2 = q2 == 2 ? 0 : q2 + 1;
+      q0 = q0 == kQTiles - 1 ? 0 : q0 + 1;
+      q2 = q2 == kQTiles - 1 ? 0 : q2 + 1;
     }
   }
 

@@ -44,6 +44,21 @@
 namespace ibwd {
 namespace {
 
+// Buffers per ring of the row kernel: K tiles, slot stages, wave 1's sign
+// words.  Gathers, stages and sign words are written a fixed number of chunks
+// ahead whatever the depth, so a build with IBWD_DEEP_BUFFERS (deeper rings, no
+// buffer reused within its window) must produce the same bits as this one;
+// the GPU tests compare the two builds.
+#ifdef IBWD_DEEP_BUFFERS
+constexpr int kKTiles = 4, kRowStages = 8, kW1Ring = 4;
+#else
+constexpr int kKTiles = 2, kRowStages = 4, kW1Ring = 2;
+#endif
+static_assert(kKTiles >= 2 && kRowStages >= 4 && kW1Ring >= 2, "rings cover the pipeline distances");
+static_assert((kKTiles & (kKTiles - 1)) == 0 && (kRowStages & (kRowStages - 1)) == 0 &&
+                  (kW1Ring & (kW1Ring - 1)) == 0,
+              "ring positions are masks of the chunk index");
+
 template <int D>
 struct ExportLds {
   // K / Q' rows are stored unpadded with their 16-byte chunks permuted by an
@@ -74,12 +89,12 @@ struct ExportLds {
     const uint2 y = tr4(tile, r1, col0);
     return u32x4_t{x.x, x.y, y.x, y.y};
   }
-  // two K tiles (chunks c, c+1); at row start each wave stages its Q' in one
-  static constexpr int kStageOff = 2 * kTile;
-  // dI (fp32), key, record position, dI - bf16(dI) (fp32); ring of 4
+  // K tiles (chunks c, c+1, ...); at row start each wave stages its Q' in one
+  static constexpr int kStageOff = kKTiles * kTile;
+  // dI (fp32), key, record position, dI - bf16(dI) (fp32); ring of kRowStages
   static constexpr int kStageBytes = kSlots * 16;
-  static constexpr int kW1Off = kStageOff + 4 * kStageBytes;  // sign words of wave 1, ring of 2
-  static constexpr int kBytes = kW1Off + 2 * kSlots * 4;
+  static constexpr int kW1Off = kStageOff + kRowStages * kStageBytes;  // sign words of wave 1
+  static constexpr int kBytes = kW1Off + kW1Ring * kSlots * 4;
 };
 
 struct Raw {
@@ -312,16 +327,16 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // ---- chunk pipeline ---------------------------------------------------------
   // Iteration c runs GEMM1 and GEMM2 of chunk c from its LDS tile, writes the
-  // K rows of chunk c+1 (gathered during iteration c-1) into the other tile
+  // K rows of chunk c+1 (gathered during iteration c-1) into its tile
   // and gathers those of chunk c+2; the gathers thus have a whole iteration to
   // land.  Each wave gathers and writes half the rows of a tile.  Slot data
-  // (dI, key) live in a ring of 4 stages written by the dI wave.  The barrier
+  // (dI, key) live in a ring of kRowStages stages written by the dI wave.  The barrier
   // at the top of an iteration publishes the tile and the stage, and the
   // record wave's view of wave 1's sign words of the previous chunk.
   const int nchunks = (n + kSlots - 1) / kSlots;
-  auto ktile = [&](int c) -> unsigned char* { return lds + (c & 1) * L::kTile; };
+  auto ktile = [&](int c) -> unsigned char* { return lds + (c & (kKTiles - 1)) * L::kTile; };
   auto stage_ptr = [&](int c) -> unsigned char* {
-    return lds + L::kStageOff + (c & 3) * L::kStageBytes;
+    return lds + L::kStageOff + (c & (kRowStages - 1)) * L::kStageBytes;
   };
   uint32_t* w1x = reinterpret_cast<uint32_t*>(lds + L::kW1Off);
   auto load_raw = [&](int c) -> Raw {
@@ -401,7 +416,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   uint32_t prev_mask = 0u;
   auto store_records = [&](int c_prev) {
     if (rec_wave && prev_valid && prev_pos >= 0) {
-      const uint32_t w1 = NG == 2 ? w1x[(c_prev & 1) * kSlots + l32] : 0u;
+      const uint32_t w1 = NG == 2 ? w1x[(c_prev & (kW1Ring - 1)) * kSlots + l32] : 0u;
       rkd[prev_pos] = prev_kd;
       rmask[prev_pos] = make_uint2(prev_mask, w1);
     }
@@ -418,7 +433,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 
   // one pipeline step: chunk c (its K tile complete), the K rows of chunk c+1
-  // into the other tile, gathers of chunk c+2
+  // into its tile, gathers of chunk c+2
   auto step = [&](int c) {
     __syncthreads();  // K tile and stage of chunk c complete; chunk c-1 done by both waves
     // raised priority while this wave issues its MFMAs, so that the other wave
@@ -477,7 +492,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
         gl[i][1] = pack_bf16(lv[2], lv[3]);
       }
     }
-    if (NG == 2 && g == 1 && lane < kSlots) w1x[(c & 1) * kSlots + lane] = maskword;
+    if (NG == 2 && g == 1 && lane < kSlots) w1x[(c & (kW1Ring - 1)) * kSlots + lane] = maskword;
 
     // ---- GEMM2: dQ'[h][d] += G'[h][j] K[j][d] ----------------------------------
     // k-step ks covers slots 16*ks + {0..15}; register e of lane (half) is slot

@@ -18,13 +18,29 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(indexer_bwd_\w+)\s*\(", src)))
 
 
-def test_library_exports_every_declared_symbol():
+@pytest.mark.parametrize("path", [ibwd.LIB_PATH, ibwd.DEEPBUF_LIB_PATH])
+def test_library_exports_every_declared_symbol(path):
+    """The library and its deep-buffer build (the verification variant)."""
     names = declared_functions()
     assert set(names) >= {"indexer_bwd_sparse", "indexer_bwd_dense", "indexer_bwd_workspace_bytes",
                           "indexer_bwd_strerror"}
-    lib = ctypes.CDLL(ibwd.LIB_PATH)
+    lib = ctypes.CDLL(path)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_using_library_switches_and_restores():
+    main = ibwd.library()
+    with ibwd.using_library(ibwd.DEEPBUF_LIB_PATH) as deep:
+        assert ibwd.library() is deep and deep is not main
+        # host-side logic is the same in both builds
+        assert ibwd.indexer_bwd_workspace_bytes(False, 1, 8192, 4096, 64, 128, 1024, 0) == \
+            main.indexer_bwd_workspace_bytes(0, 1, 8192, 4096, 64, 128, 1024, 0)
+    assert ibwd.library() is main
+    with pytest.raises(RuntimeError):
+        with ibwd.using_library("/nonexistent/libdsa_indexer_bwd.so"):
+            pass
+    assert ibwd.library() is main
 
 
 def test_strerror_and_workspace():
