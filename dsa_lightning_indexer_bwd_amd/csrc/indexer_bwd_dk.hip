@@ -17,21 +17,23 @@
 //   A_t[key][h] = dI of t's record of key  *  its sign bit of head h
 //                 (0 when t has no record of key),  Q'_t = (w*q)^T of row t.
 //
-//   workgroup (key range of 128 keys, query block, batch), four waves: wave
-//   (kh, ch) owns keys 64kh .. 64kh+63 and columns D/2*ch .. of the range, as
-//   v_mfma 32x32x16 accumulators (64 fp32 registers per lane at D = 128).
-//   Per query with records in the range: wave 0 scatters the records into a
-//   key table in LDS ({dI, sign words, tag}; entries of other queries are told
-//   apart by the tag, so the table is never cleared), the four waves DMA
-//   Q'_t into LDS (global_load_lds, 16 bytes per lane, rows XOR-swizzled so
-//   the 16-byte B-operand reads are bank-conflict free), one barrier, then
-//   every wave expands its A fragments from the table (bf16 dI where the sign
-//   bit is set, three VALU operations per pair of heads) and issues its
-//   MFMAs.  Q' tiles are copied two queries ahead (three tiles), record stages
-//   three ahead (four stages) and key tables built one ahead (two tables), so
-//   the next queries' copies and scatter run while the current one computes.
+//   workgroup (key range of 128 keys, query block, batch): four MMA waves and
+//   a producer wave.  MMA wave (kh, ch) owns keys 64kh .. 64kh+63 and columns
+//   D/2*ch .. of the range, as v_mfma 32x32x16 accumulators (64 fp32 registers
+//   per lane at D = 128).  Per query with records in the range the producer
+//   copies the query's records and Q'_t into LDS (global_load_lds, 16 bytes
+//   per lane; Q' rows XOR-swizzled so the 16-byte B-operand reads are
+//   bank-conflict free) and scatters the records into a key table ({dI, sign
+//   words, tag}; entries of other queries are told apart by the tag, so the
+//   table is never cleared); after one barrier every MMA wave expands its A
+//   fragments from the table (bf16 dI where the sign bit is set, three VALU
+//   operations per pair of heads) and issues its MFMAs.  Q' tiles are copied
+//   two queries ahead (three tiles), record stages three ahead (four stages)
+//   and key tables built one ahead (two tables), so the next queries' copies
+//   and scatter run while the current one computes; the MMA waves issue no
+//   memory operation but their B reads and table reads.
 //   A key that a row selects twice (duplicate ids) keeps one record in the
-//   table; wave 0 notices the other by reading the tags back, and after the
+//   table; the producer notices the other by reading the tags back, and after the
 //   query loop the workgroup adds every such record in a pass of its own, in
 //   a fixed order, so the result stays deterministic.
 //   The MFMA work is 2*H*D per (query, key of the range) whether the query
@@ -87,11 +89,10 @@ struct DkShape {
   static constexpr int kFlagOff = kListOff + kMaxQueryBlock * 16;
   static constexpr int kBytes = kFlagOff + 16;
   static constexpr int kDmaQ = kQBytes / 1024;  // copies of 64 lanes x 16 B per Q' tile
-  static constexpr int kDmaW = kDmaQ / NW;       // ... issued by each MMA wave
   static constexpr int kFbTag = 16382;         // pass id of the duplicate passes
   // (query passes use 0 .. kMaxQueryBlock-1; 16383 marks a never-written entry)
-  static_assert(kDmaW * NW * 1024 == kQBytes, "Q' tile splits into whole copies per wave");
-  static_assert(kDmaW < 64, "one iteration's copies fit a vmcnt immediate");
+  static_assert(kDmaQ * 1024 == kQBytes, "Q' tile splits into whole copies");
+  static_assert(kDmaQ + 2 < 64, "one iteration's copies fit a vmcnt immediate");
   static_assert(kQTiles * kQBytes >= kMaxQueryBlock * 4, "Q' tiles double as scan scratch");
   static_assert(kRecBlock * 8 == 1024, "one DMA moves a record block of one array");
   static_assert(KBW * 32 * NWK == RK, "key blocks cover the range");
@@ -251,9 +252,9 @@ dk_range_kernel(Problem P) {
   auto stage_w = [&](int buf) {
     return reinterpret_cast<const uint2*>(lds + S::kStOff + buf * S::kStBytes + kRecBlock * 8);
   };
-  // MMA wave wv: its kDmaW KiB of Q'_t of row `row` into tile `buf`; lane i
-  // of each copy fills LDS bytes 16i.. of its KiB with the global chunk the
-  // XOR swizzle puts there (the swizzle term depends on the lane only)
+  // lane i of each copy of a Q' tile fills LDS bytes 16i.. of its KiB with the
+  // global chunk the XOR swizzle puts there (the swizzle term depends on the
+  // lane only)
   uint32_t dma_lane;
   {
     const int pl = 16 * lane;
@@ -261,14 +262,13 @@ dk_range_kernel(Problem P) {
     const int f = (pl >> 7) & (S::kCpr - 1);
     dma_lane = uint32_t((pl & ~(S::kRowBytes - 1)) | ((c ^ f) << 4));
   }
+  // producer: all of Q'_t of row `row` into tile `buf`
   auto dma_qt = [&](int row, int buf) {
     const unsigned char* src =
         reinterpret_cast<const unsigned char*>(P.qt) + size_t(uni(row)) * S::kQBytes;
 #pragma unroll
-    for (int j = 0; j < S::kDmaW; ++j) {
-      const int kib = wv * S::kDmaW + j;
+    for (int kib = 0; kib < S::kDmaQ; ++kib)
       dma16(lds0 + uint32_t(buf * S::kQBytes + kib * 1024), src + kib * 1024, dma_lane);
-    }
   };
   // producer: records first .. first+kRecBlock-1 of row `row` into stage `buf`
   // (two DMAs: {key, dI} and the sign words; records past the range's end are
@@ -371,20 +371,25 @@ dk_range_kernel(Problem P) {
   };
 
   // ---- query loop ---------------------------------------------------------------
-  // Query qi: Q' tile qi % kQTiles (copied two queries ahead by the MMA
-  // waves), record stage qi % kStages (copied three queries ahead by the
-  // producer), key table qi % kTables (built by the producer right after the barrier of query
-  // qi-1, from the staged records).  Every wave issues its copies and no other
-  // vector-memory operation in the loop (except the producer's loads of
-  // records past a staged block, which the compiler waits for at once), so
-  // "all but the previous iteration's copies" is one vmcnt immediate.  The
-  // two roles run separate loops (so that their registers need not be live at
-  // once), each with one barrier per query.
+  // Query qi: Q' tile qi % kQTiles (copied two queries ahead), record stage
+  // qi % kStages (copied three queries ahead), key table qi % kTables (built
+  // right after the barrier of query qi-1, from the staged records), all by
+  // the producer.  The producer issues its copies and no other vector-memory
+  // operation in the loop (except its loads of records past a staged block,
+  // which the compiler waits for at once), so "all but the previous
+  // iteration's copies" is one vmcnt immediate.  The two roles run separate
+  // loops (so that their registers need not be live at once), each with one
+  // barrier per query.
   bool dup = false;  // producer: some record lost its table entry to a duplicate key
   if (prod) {
-    auto wait_prev = [&](bool issued) {
-      if (issued)
-        wait_vm<2>();
+    // Iteration j copies Q'(j+2) and then records(j+3); at the top of
+    // iteration qi every copy but those of iteration qi-1 must have landed
+    // (Q'(qi) and records(qi+1) among them).
+    auto wait_prev = [&](int qi) {
+      if (qi + 2 < nne)
+        wait_vm<S::kDmaQ + 2>();
+      else if (qi + 1 < nne)
+        wait_vm<S::kDmaQ>();
       else
         wait_vm<0>();
     };
@@ -392,25 +397,28 @@ dk_range_kernel(Problem P) {
     if (nne > 0) {
       const int4 e0 = list[0];
       dma_recs(e0.x, e0.y, 0);
-      if (nne > 1) dma_recs(uni(list[1].x), uni(list[1].y), 1);
-      // the copy of "iteration -1": records(2)
-      if (nne > 2) dma_recs(uni(list[2].x), uni(list[2].y), 2);
-      wait_prev(nne > 2);  // records(0), records(1) are in
+      wait_vm<0>();
       scatter(e0, 0, 0, 0, key);
+      // the copies of "iterations" -2 and -1
+      dma_qt(e0.x, 0);
+      if (nne > 1) dma_recs(uni(list[1].x), uni(list[1].y), 1);
+      if (nne > 1) dma_qt(uni(list[1].x), 1);
+      if (nne > 2) dma_recs(uni(list[2].x), uni(list[2].y), 2);
     }
     // list entries are read one iteration before they are needed
     int4 e_cur = nne > 0 ? list[0] : make_int4(0, 0, 0, 0);
     int4 e_n1 = nne > 1 ? list[1] : e_cur;
+    int4 e_n2 = nne > 2 ? list[2] : e_cur;
     int4 e_n3 = nne > 3 ? list[3] : e_cur;
+    int q2 = 2 % kQTiles;  // (qi+2) % kQTiles
     for (int qi = 0; qi < nne; ++qi) {
-      // the copy of iteration qi-1 is records(qi+2) if qi+2 < nne; records(qi+1)
-      // is in
-      wait_prev(qi + 2 < nne);
-      __syncthreads();  // table qi % kTables is complete; query qi-1 is done
-      const int4 e1 = e_n1, e3 = e_n3;
+      wait_prev(qi);
+      __syncthreads();  // Q'(qi) and table qi % kTables are complete; query qi-1 is done
+      const int4 e1 = e_n1, e2 = e_n2, e3 = e_n3;
       const int n = uni(e_cur.z) - uni(e_cur.y);
       e_cur = e1;
-      if (qi + 2 < nne) e_n1 = list[qi + 2];
+      e_n1 = e2;
+      e_n2 = e3;
       if (qi + 4 < nne) e_n3 = list[qi + 4];
       // duplicates of query qi: read its table entries back (its table stays
       // intact until the scatter of query qi+2, one iteration later)
@@ -419,6 +427,9 @@ dk_range_kernel(Problem P) {
       // the MMA waves wait for this table at the next barrier: the producer's
       // work of the iteration runs at the highest priority of the CU's waves
       __builtin_amdgcn_s_setprio(2);
+      // Q' tile (qi+2) % kQTiles was last read in query qi-1 at the latest
+      if (qi + 2 < nne) dma_qt(e2.x, q2);
+      q2 = q2 == kQTiles - 1 ? 0 : q2 + 1;
       if (qi + 1 < nne) scatter(e1, (qi + 1) % kStages, (qi + 1) % kTables, qi + 1, key);
       dup = dup || lost_any(n, kq, qi % kTables, qi);
       // stage (qi+3) % kStages was last read at the latest by the scatter of query
@@ -427,35 +438,15 @@ dk_range_kernel(Problem P) {
       __builtin_amdgcn_s_setprio(0);
     }
   } else {
-    auto wait_prev = [&](bool issued) {
-      if (issued)
-        wait_vm<S::kDmaW>();
-      else
-        wait_vm<0>();
-    };
-    if (nne > 0) {
-      dma_qt(list[0].x, 0);
-      // the copy of "iteration -1": Q'(1)
-      if (nne > 1) dma_qt(list[1].x, 1);
-    }
-    int q0 = 0, q2 = 2;  // qi % kQTiles, (qi+2) % kQTiles
-    int row2 = nne > 2 ? list[2].x : 0;  // read one iteration before it is needed
+    int q0 = 0;  // qi % kQTiles
     for (int qi = 0; qi < nne; ++qi) {
-      // the copy of iteration qi-1 is Q'(qi+1) if qi+1 < nne; this wave's
-      // share of Q'(qi) is in
-      wait_prev(qi + 1 < nne);
-      __syncthreads();  // every share of Q'(qi), and table qi % kTables, are complete
-      // Q' tile (qi+2) % kQTiles was last read in query qi-1 at the latest
-      const int r2 = row2;
-      if (qi + 3 < nne) row2 = list[qi + 3].x;
-      if (qi + 2 < nne) dma_qt(r2, q2);
+      __syncthreads();  // Q'(qi) and table qi % kTables are complete
       // raised priority while this wave expands and issues its MFMAs, so that
       // the other MMA wave of the SIMD fills the gaps with its own work
       __builtin_amdgcn_s_setprio(1);
       mfma_pass(qi % kTables, q0, qi);
       __builtin_amdgcn_s_setprio(0);
       q0 = q0 == kQTiles - 1 ? 0 : q0 + 1;
-      q2 = q2 == kQTiles - 1 ? 0 : q2 + 1;
     }
   }
 
@@ -473,12 +464,10 @@ dk_range_kernel(Problem P) {
       const int4 e = list[qi];
       if (prod) {
         dma_recs(e.x, e.y, 0);
+        dma_qt(e.x, 0);
         wait_vm<0>();
         int kq[2];
         scatter(e, 0, 0, S::kFbTag, kq);
-      } else {
-        dma_qt(e.x, 0);
-        wait_vm<0>();
       }
       __syncthreads();
       const int n = uni(e.z) - uni(e.y);
