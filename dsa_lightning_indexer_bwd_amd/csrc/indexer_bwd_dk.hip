@@ -153,6 +153,25 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* gbase, uint
       : "memory");
 }
 
+// Four such copies of consecutive KiBs: global gbase + voff + 1024k into LDS
+// lds_addr + 16*lane + 1024k, k = 0..3, under one M0 (the instruction offset
+// moves the global address and the LDS destination alike).
+__device__ __forceinline__ void dma16x4(uint32_t lds_addr, const void* gbase, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:1024\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:2048\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:3072\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(gbase)
+      : "memory");
+}
+
 // Byte offset of chunk (16 bytes) c of row d of a Q' tile in LDS: the chunk
 // index is XORed with bits of the row so that eight consecutive rows read at
 // one chunk (one 16-byte B-operand read of eight lanes) hit distinct banks.
@@ -262,13 +281,17 @@ dk_range_kernel(Problem P) {
     const int f = (pl >> 7) & (S::kCpr - 1);
     dma_lane = uint32_t((pl & ~(S::kRowBytes - 1)) | ((c ^ f) << 4));
   }
-  // producer: all of Q'_t of row `row` into tile `buf`
+  // producer: all of Q'_t of row `row` into tile `buf`, four KiB per M0 setting
   auto dma_qt = [&](int row, int buf) {
     const unsigned char* src =
         reinterpret_cast<const unsigned char*>(P.qt) + size_t(uni(row)) * S::kQBytes;
+    const uint32_t dst = lds0 + uint32_t(buf * S::kQBytes);
 #pragma unroll
-    for (int kib = 0; kib < S::kDmaQ; ++kib)
-      dma16(lds0 + uint32_t(buf * S::kQBytes + kib * 1024), src + kib * 1024, dma_lane);
+    for (int kib = 0; kib + 4 <= S::kDmaQ; kib += 4)
+      dma16x4(dst + uint32_t(kib * 1024), src + kib * 1024, dma_lane);
+#pragma unroll
+    for (int kib = S::kDmaQ & ~3; kib < S::kDmaQ; ++kib)
+      dma16(dst + uint32_t(kib * 1024), src + kib * 1024, dma_lane);
   };
   // producer: records first .. first+kRecBlock-1 of row `row` into stage `buf`
   // (two DMAs: {key, dI} and the sign words; records past the range's end are
