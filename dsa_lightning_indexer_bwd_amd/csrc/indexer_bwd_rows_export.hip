@@ -297,6 +297,17 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   for (int kd = 0; kd < KD; ++kd)
     qb1[kd] = hl < H ? *reinterpret_cast<const u32x4_t*>(qrow + hl * D + 8 * half + 16 * kd)
                      : u32x4_t{0u, 0u, 0u, 0u};
+  // the first two chunks' slot loads, issued now so that their latency
+  // overlaps the (w*q)^T work below
+  auto load_raw = [&](int c) -> Raw {
+    const int j = c * kSlots + l32;
+    const int jc = j < row_len ? j : row_len - 1;
+    Raw v;
+    v.id = DENSE ? 0 : idrow[jc];
+    v.pd = slotrow[jc];
+    return v;
+  };
+  const Raw raw0 = load_raw(0), raw1 = load_raw(1);
   // (w*q)^T: Q' rows staged in LDS (K tile g of this wave) at the natural head
   // offset rotl5(l32), read back transposed (lane d = 32*nd + l32, 8 heads
   // from 16*ks + 8*half)
@@ -339,14 +350,6 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     return lds + L::kStageOff + (c & (kRowStages - 1)) * L::kStageBytes;
   };
   uint32_t* w1x = reinterpret_cast<uint32_t*>(lds + L::kW1Off);
-  auto load_raw = [&](int c) -> Raw {
-    const int j = c * kSlots + l32;
-    const int jc = j < row_len ? j : row_len - 1;
-    Raw v;
-    v.id = DENSE ? 0 : idrow[jc];
-    v.pd = slotrow[jc];
-    return v;
-  };
   // key of the lane's slot; the dI wave also publishes dI and key, the record
   // wave the position of the slot's record (lanes l and l+32 write the same
   // values)
@@ -425,10 +428,9 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   u32x4_t kr[NCH];
   Raw raw;
   if (nchunks > 0) {
-    gather(finalize(0, load_raw(0)), kr);
-    raw = load_raw(1);
+    gather(finalize(0, raw0), kr);
     store_ktile(0, kr);
-    gather(finalize(1, raw), kr);
+    gather(finalize(1, raw1), kr);
     raw = load_raw(2);
   }
 
