@@ -412,10 +412,21 @@ def read_gfx_clock():
     accelerator dies' current clocks, "max_mhz": their rated maximum}, or None
     when amd-smi is unavailable.  The clocks drop to a few hundred MHz when the
     GPU idles, so a sample means something only while kernels run."""
+    import shutil
     import subprocess
 
     try:
-        res = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
+        # amd-smi is a Python script started through `env`; running it with this
+        # interpreter directly keeps the child from replacing itself once more
+        # (a profiler's preloaded library may have initialised the GPU in it)
+        tool = shutil.which("amd-smi")
+        if tool is None:
+            return None
+        tool = os.path.realpath(tool)
+        with open(tool, "rb") as f:
+            head = f.readline()
+        cmd = [sys.executable, tool] if b"python" in head else [tool]
+        res = subprocess.run(cmd + ["metric", "-c", "--json"], capture_output=True, text=True,
                              timeout=20)
         start = res.stdout.find("{")
         data = json.loads(res.stdout[start:]) if start >= 0 else None
