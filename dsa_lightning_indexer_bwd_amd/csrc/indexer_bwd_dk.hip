@@ -183,9 +183,11 @@ __device__ __forceinline__ int qt_swz(int d, int c) {
 }
 
 template <int NH, int D>
-// Two workgroups of NW + 1 waves share a CU: three waves per SIMD, so at most
-// 168 registers per lane.
-__global__ __launch_bounds__((DkShape<D, NH * 32>::NTH)) __attribute__((amdgpu_waves_per_eu(3))) void
+// Two workgroups of NW + 1 waves share a CU (three waves on two of the SIMDs,
+// two on the others), but the kernel is held to 128 registers per lane, the
+// budget of four waves per SIMD: measured at the 8192 x 1024 workload, the
+// same code given 136 registers runs 30% slower.
+__global__ __launch_bounds__((DkShape<D, NH * 32>::NTH)) __attribute__((amdgpu_waves_per_eu(4))) void
 dk_range_kernel(Problem P) {
   constexpr int HP = NH * 32;
   using S = DkShape<D, HP>;
@@ -337,7 +339,10 @@ dk_range_kernel(Problem P) {
       const bool valid = (e.w >> 18) == uint32_t(pid);
       // bf16 dI where the sign bit is set: ((word >> p) & 0x10001) * dI_bf16
       // puts dI in both halves of a pair of heads at once
-      const uint32_t dib = valid ? (pack_bf16(__uint_as_float(e.x), 0.f) & 0xffffu) : 0u;
+      // (a 24-bit multiply by 0 or 1, not a select: the compiler turns such a
+      // select into a branch around a second read of the entry's dI, a
+      // dependent LDS round trip in the middle of the pass)
+      const uint32_t dib = __umul24(pack_bf16(__uint_as_float(e.x), 0.f) & 0xffffu, uint32_t(valid));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const uint32_t word = (ks < 2 ? e.y : e.z) >> (8 * (ks & 1) + 4 * half);
@@ -484,25 +489,29 @@ dk_range_kernel(Problem P) {
     for (int i = tid; i < 2 * RK; i += NTH) table(0)[i] = make_uint4(0, 0, 0, 0xffffffffu);
     for (int qi = 0; qi < nne; ++qi) {
       __syncthreads();
-      const int4 e = list[qi];
+      // the entry's fields in scalar registers: they stay live across the passes
+      const int4 el = list[qi];
+      const int ex = uni(el.x), ey = uni(el.y), n = uni(el.z) - ey;
       if (prod) {
-        dma_recs(e.x, e.y, 0);
-        dma_qt(e.x, 0);
+        dma_recs(ex, ey, 0);
+        dma_qt(ex, 0);
         wait_vm<0>();
         int kq[2];
-        scatter(e, 0, 0, S::kFbTag, kq);
+        scatter(make_int4(ex, ey, ey + n, 0), 0, 0, S::kFbTag, kq);
       }
       __syncthreads();
-      const int n = uni(e.z) - uni(e.y);
       for (int c0 = 0; c0 < n; c0 += 64) {
         if (prod) {
           bool lost = false;
           if (c0 + lane < n) {
-            const int2 kd = rec_kd(e.x, e.y + c0 + lane);
+            const int2 kd = rec_kd(ex, ey + c0 + lane);
             lost = table(0)[(kd.x - R0) & (RK - 1)].w != tag_of(S::kFbTag, c0 + lane);
           }
           const uint64_t m = ballot(lost);
-          if (lost) losers[__popcll(m & lanemask_lt())] = c0 + lane;
+          // (position among the lost lanes below this one)
+          const int pos = int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+          if (lost) losers[pos] = c0 + lane;
           if (lane == 0) flags[2] = __popcll(m);
         }
         __syncthreads();
@@ -510,8 +519,8 @@ dk_range_kernel(Problem P) {
         for (int li = 0; li < nl; ++li) {
           const int r = uni(losers[li]);
           if (prod && lane == 0) {
-            const int2 kd = rec_kd(e.x, e.y + r);
-            const uint2 w = rec_w(e.x, e.y + r);
+            const int2 kd = rec_kd(ex, ey + r);
+            const uint2 w = rec_w(ex, ey + r);
             table(1)[(kd.x - R0) & (RK - 1)] =
                 make_uint4(uint32_t(kd.y), w.x, w.y, tag_of(S::kFbTag, r));
           }
@@ -519,7 +528,7 @@ dk_range_kernel(Problem P) {
           if (!prod) mfma_pass(1, 0, S::kFbTag);
           __syncthreads();
           if (prod && lane == 0)
-            table(1)[(rec_kd(e.x, e.y + r).x - R0) & (RK - 1)] = make_uint4(0, 0, 0, 0xffffffffu);
+            table(1)[(rec_kd(ex, ey + r).x - R0) & (RK - 1)] = make_uint4(0, 0, 0, 0xffffffffu);
         }
         __syncthreads();
       }
