@@ -18,9 +18,9 @@
 //                 (0 when t has no record of key),  Q'_t = (w*q)^T of row t.
 //
 //   workgroup (key range of 128 keys, query block, batch): four MMA waves and
-//   a producer wave.  MMA wave (kh, ch) owns keys 64kh .. 64kh+63 and columns
-//   D/2*ch .. of the range, as v_mfma 32x32x16 accumulators (64 fp32 registers
-//   per lane at D = 128).  Per query with records in the range the producer
+//   a producer wave.  MMA wave kh owns keys 32kh .. 32kh+31 and all D columns
+//   of the range, as v_mfma 32x32x16 accumulators (64 fp32 registers per lane
+//   at D = 128), so each A fragment it expands serves D/32 MFMAs.  Per query with records in the range the producer
 //   copies the query's records and Q'_t into LDS (global_load_lds, 16 bytes
 //   per lane; Q' rows XOR-swizzled so the 16-byte B-operand reads are
 //   bank-conflict free) and scatters the records into a key table ({dI, sign
@@ -72,8 +72,8 @@ template <int D, int HP>
 struct DkShape {
   static constexpr int RK = kRangeKeys;        // keys per range (4 blocks of 32)
   static constexpr int NCB = D / 32;           // 32-column blocks
-  static constexpr int NWC = NCB >= 2 ? 2 : 1; // column groups of waves
-  static constexpr int NWK = 2;                // key groups of waves
+  static constexpr int NWC = 1;                // column groups of waves
+  static constexpr int NWK = 4;                // key groups of waves (one 32-key block each)
   static constexpr int NW = NWK * NWC;         // MMA waves (plus one producer wave)
   static constexpr int NTH = 64 * (NW + 1);
   static constexpr int KBW = RK / 32 / NWK;    // key blocks per wave
@@ -95,7 +95,7 @@ struct DkShape {
   static_assert(kDmaQ + 2 < 64, "one iteration's copies fit a vmcnt immediate");
   static_assert(kQTiles * kQBytes >= kMaxQueryBlock * 4, "Q' tiles double as scan scratch");
   static_assert(kRecBlock * 8 == 1024, "one DMA moves a record block of one array");
-  static_assert(KBW * 32 * NWK == RK, "key blocks cover the range");
+  static_assert(KBW == 1 && 32 * NWK == RK, "one 32-key block per MMA wave");
 };
 
 // Exclusive prefix sum over a[0..n) in LDS by one wave, in place; returns the total.
@@ -202,9 +202,9 @@ dk_range_kernel(Problem P) {
   const int l32 = lane & 31;
   const int half = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // waves 0 .. NW-1 own keys 64kh.. x columns .. and copy Q' tiles into LDS;
-  // wave NW produces the key tables (copies the records, scatters them,
-  // checks for duplicate keys) and does no MMA
+  // waves 0 .. NW-1 own keys 32kh .. 32kh+31 x all columns;
+  // wave NW copies the records and Q' tiles, builds the key tables (scatters
+  // the records, checks for duplicate keys) and does no MMA
   const bool prod = wv == S::NW;
   const int kh = wv % S::NWK, ch = (wv / S::NWK) % S::NWC;
   // Workgroup i is dispatched to XCD i % 8.  Consecutive logical ids (the key
@@ -313,7 +313,7 @@ dk_range_kernel(Problem P) {
   auto tag_of = [](int pid, int r) { return uint32_t(pid) << 18 | uint32_t(r); };
 
   // accumulators: key block kb (keys 32*(KBW*kh + kb) + 8i + 4half + r in
-  // register 4i + r), column block cb (column 32*(CBW*ch + cb) + l32)
+  // register 4i + r; KBW = 1), column block cb (column 32*(CBW*ch + cb) + l32)
   f32x16_t acc[S::KBW][S::CBW];
 #pragma unroll
   for (int kb = 0; kb < S::KBW; ++kb)
@@ -321,37 +321,30 @@ dk_range_kernel(Problem P) {
     for (int cb = 0; cb < S::CBW; ++cb) acc[kb][cb] = f32x16_t{};
 
   // one query's (or one duplicate record's) contribution: A from key table
-  // `tb` (entries tagged with pass `pid`), B = Q' tile `qbuf`
+  // `tb` (entries tagged with pass `pid`), B = Q' tile `qbuf`.  The wave's A
+  // fragment of a k-step (its 32 keys x 16 heads) serves all its column blocks.
   auto mfma_pass = [&](int tb, int qbuf, int pid) {
-    const uint4* T = table(tb);
+    const uint4 e = table(tb)[32 * kh + l32];
     const unsigned char* Q = qtile(qbuf);
-    u32x4_t bop[S::CBW][KS];
+    const bool valid = (e.w >> 18) == uint32_t(pid);
+    // bf16 dI where the sign bit is set: ((word >> p) & 0x10001) * dI_bf16
+    // puts dI in both halves of a pair of heads at once
+    // (a 24-bit multiply by 0 or 1, not a select: the compiler turns such a
+    // select into a branch around a second read of the entry's dI, a
+    // dependent LDS round trip in the middle of the pass)
+    const uint32_t dib = __umul24(pack_bf16(__uint_as_float(e.x), 0.f) & 0xffffu, uint32_t(valid));
 #pragma unroll
-    for (int cb = 0; cb < S::CBW; ++cb) {
-      const int d = 32 * (S::CBW * ch + cb) + l32;
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t b[S::CBW];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        bop[cb][ks] = *reinterpret_cast<const u32x4_t*>(Q + qt_swz<HP>(d, 2 * ks + half));
-    }
+      for (int cb = 0; cb < S::CBW; ++cb)
+        b[cb] = *reinterpret_cast<const u32x4_t*>(Q + qt_swz<HP>(32 * (S::CBW * ch + cb) + l32, 2 * ks + half));
+      const uint32_t word = (ks < 2 ? e.y : e.z) >> (8 * (ks & 1) + 4 * half);
+      u32x4_t a;
 #pragma unroll
-    for (int kb = 0; kb < S::KBW; ++kb) {
-      const uint4 e = T[32 * (S::KBW * kh + kb) + l32];
-      const bool valid = (e.w >> 18) == uint32_t(pid);
-      // bf16 dI where the sign bit is set: ((word >> p) & 0x10001) * dI_bf16
-      // puts dI in both halves of a pair of heads at once
-      // (a 24-bit multiply by 0 or 1, not a select: the compiler turns such a
-      // select into a branch around a second read of the entry's dI, a
-      // dependent LDS round trip in the middle of the pass)
-      const uint32_t dib = __umul24(pack_bf16(__uint_as_float(e.x), 0.f) & 0xffffu, uint32_t(valid));
+      for (int j = 0; j < 4; ++j) a[j] = __umul24((word >> j) & 0x10001u, dib);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t word = (ks < 2 ? e.y : e.z) >> (8 * (ks & 1) + 4 * half);
-        u32x4_t a;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = __umul24((word >> j) & 0x10001u, dib);
-#pragma unroll
-        for (int cb = 0; cb < S::CBW; ++cb) acc[kb][cb] = mfma32(a, bop[cb][ks], acc[kb][cb]);
-      }
+      for (int cb = 0; cb < S::CBW; ++cb) acc[0][cb] = mfma32(a, b[cb], acc[0][cb]);
     }
   };
 
