@@ -182,7 +182,10 @@ __device__ __forceinline__ int qt_swz(int d, int c) {
   return d * HP * 2 + ((c ^ f) << 4);
 }
 
-template <int NH, int D>
+// SKIP: an MMA wave passes over a query that has no record among its 32 keys
+// (worth it only when a query averages at most about one record per 32 keys:
+// the test delays the wave's B reads behind its table read).
+template <int NH, int D, bool SKIP>
 // Two workgroups of NW + 1 waves share a CU (three waves on two of the SIMDs,
 // two on the others), but the kernel is held to 128 registers per lane, the
 // budget of four waves per SIMD: measured at the 8192 x 1024 workload, the
@@ -333,6 +336,7 @@ dk_range_kernel(Problem P) {
     // select into a branch around a second read of the entry's dI, a
     // dependent LDS round trip in the middle of the pass)
     const uint32_t dib = __umul24(pack_bf16(__uint_as_float(e.x), 0.f) & 0xffffu, uint32_t(valid));
+    if (SKIP && ballot(valid) == 0) return;  // no record of this query among the wave's keys
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t b[S::CBW];
@@ -572,15 +576,23 @@ __global__ __launch_bounds__(256) void dk_sum_kernel(Problem P) {
   }
 }
 
-template <int NH, int D>
-hipError_t launch_dk_t(const Problem& P, hipStream_t stream) {
+template <int NH, int D, bool SKIP>
+hipError_t launch_range(const Problem& P, hipStream_t stream) {
   using S = DkShape<D, NH * 32>;
   const dim3 grid(unsigned(P.NR * P.NQB * P.B));
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&dk_range_kernel<NH, D>),
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&dk_range_kernel<NH, D, SKIP>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::kBytes);
   if (err != hipSuccess) return err;
-  dk_range_kernel<NH, D><<<grid, S::NTH, S::kBytes, stream>>>(P);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  dk_range_kernel<NH, D, SKIP><<<grid, S::NTH, S::kBytes, stream>>>(P);
+  return hipGetLastError();
+}
+
+template <int NH, int D>
+hipError_t launch_dk_t(const Problem& P, hipStream_t stream) {
+  // skipping pays when a row averages at most one slot per 32 keys
+  const bool skip = !P.dense && P.row_len * 32 <= P.S_k;
+  hipError_t err = skip ? launch_range<NH, D, true>(P, stream) : launch_range<NH, D, false>(P, stream);
+  if (err != hipSuccess) return err;
   stage_done(2, "dk_range_kernel");
   const int64_t n4 = P.B * P.S_k * P.D / 4;
   int64_t blocks = (n4 + 255) / 256;

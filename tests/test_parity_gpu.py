@@ -316,12 +316,15 @@ def test_atomic_route(ibwd, name):
 
 
 @pytest.mark.parametrize("atomic_dk", [False, True])
-def test_duplicate_ids(ibwd, atomic_dk):
+@pytest.mark.parametrize("S_k,topk", [(300, 200), (4096, 96)])
+def test_duplicate_ids(ibwd, atomic_dk, S_k, topk):
     """Duplicate ids in a row are independent slots (both routes; the default
-    route's range kernel takes its ordered path for tiles with repeated keys)."""
-    log(f"case: duplicate ids atomic={atomic_dk}")
-    wl = dataclasses.replace(WORKLOADS["anchor"], S_q=48, S_k=300, topk=200, pad_frac=0.05)
-    x = make_inputs(wl, seed=31)
+    route's range kernel takes its ordered path for tiles with repeated keys).
+    At 96 of 4096 keys the range kernel's waves also pass over key blocks
+    without a record of the query."""
+    log(f"case: duplicate ids atomic={atomic_dk} S_k={S_k} topk={topk}")
+    wl = dataclasses.replace(WORKLOADS["anchor"], S_q=48, S_k=S_k, topk=topk, pad_frac=0.05)
+    x = make_inputs(wl, seed=31 + topk)
     rng = np.random.default_rng(5)
     # every row: a third of its slots repeat keys of the row (some several times)
     for t in range(wl.S_q):
@@ -330,7 +333,7 @@ def test_duplicate_ids(ibwd, atomic_dk):
         x.ids[0, t, dst] = x.ids[0, t, src]
     x.ids[0, 0, :] = 7          # a row of one key repeated
     got = run(ibwd, x, atomic_dk=atomic_dk)
-    assert_parity(f"dup-atomic{int(atomic_dk)}", got, oracle.Problem.from_inputs(x).backward())
+    assert_parity(f"dup-atomic{int(atomic_dk)}-{S_k}", got, oracle.Problem.from_inputs(x).backward())
 
 
 def test_ragged_row_lengths(ibwd):
