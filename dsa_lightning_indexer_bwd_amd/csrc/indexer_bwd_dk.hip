@@ -286,18 +286,21 @@ dk_range_kernel(Problem P) {
     const int f = (pl >> 7) & (S::kCpr - 1);
     dma_lane = uint32_t((pl & ~(S::kRowBytes - 1)) | ((c ^ f) << 4));
   }
-  // producer: all of Q'_t of row `row` into tile `buf`, four KiB per M0 setting
-  auto dma_qt = [&](int row, int buf) {
+  // producer: KiBs k0 .. k1-1 of Q'_t of row `row` into tile `buf`, four KiB
+  // per M0 setting
+  auto dma_qt_part = [&](int row, int buf, int k0, int k1) {
     const unsigned char* src =
         reinterpret_cast<const unsigned char*>(P.qt) + size_t(uni(row)) * S::kQBytes;
     const uint32_t dst = lds0 + uint32_t(buf * S::kQBytes);
+    int kib = k0;
 #pragma unroll
-    for (int kib = 0; kib + 4 <= S::kDmaQ; kib += 4)
-      dma16x4(dst + uint32_t(kib * 1024), src + kib * 1024, dma_lane);
+    for (; kib + 4 <= k1; kib += 4) dma16x4(dst + uint32_t(kib * 1024), src + kib * 1024, dma_lane);
 #pragma unroll
-    for (int kib = S::kDmaQ & ~3; kib < S::kDmaQ; ++kib)
-      dma16(dst + uint32_t(kib * 1024), src + kib * 1024, dma_lane);
+    for (; kib < k1; ++kib) dma16(dst + uint32_t(kib * 1024), src + kib * 1024, dma_lane);
   };
+  auto dma_qt = [&](int row, int buf) { dma_qt_part(row, buf, 0, S::kDmaQ); };
+  // the loop issues a tile's copies in two parts (a multiple of four KiB first)
+  constexpr int kQSplit = S::kDmaQ >= 8 ? (S::kDmaQ / 2) & ~3 : S::kDmaQ / 2;
   // producer: records first .. first+kRecBlock-1 of row `row` into stage `buf`
   // (two DMAs: {key, dI} and the sign words; records past the range's end are
   // read and ignored)
@@ -452,11 +455,15 @@ dk_range_kernel(Problem P) {
       // the MMA waves wait for this table at the next barrier: the producer's
       // work of the iteration runs at the highest priority of the CU's waves
       __builtin_amdgcn_s_setprio(2);
-      // Q' tile (qi+2) % kQTiles was last read in query qi-1 at the latest
-      if (qi + 2 < nne) dma_qt(e2.x, q2);
-      q2 = q2 == kQTiles - 1 ? 0 : q2 + 1;
+      // The scatter and the tag check are chains of LDS round trips; the copies
+      // are issued around the tag check, where they wait on the copy queue
+      // while those round trips are in flight.
       if (qi + 1 < nne) scatter(e1, (qi + 1) % kStages, (qi + 1) % kTables, qi + 1, key);
+      // Q' tile (qi+2) % kQTiles was last read in query qi-1 at the latest
+      if (qi + 2 < nne) dma_qt_part(e2.x, q2, 0, kQSplit);
       dup = dup || lost_any(n, kq, qi % kTables, qi);
+      if (qi + 2 < nne) dma_qt_part(e2.x, q2, kQSplit, S::kDmaQ);
+      q2 = q2 == kQTiles - 1 ? 0 : q2 + 1;
       // stage (qi+3) % kStages was last read at the latest by the scatter of query
       // qi-1, whose table writes waited for those reads
       if (qi + 3 < nne) dma_recs(uni(e3.x), uni(e3.y), (qi + 3) % kStages);
