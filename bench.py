@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--atomic-dk", action="store_true",
                     help="the single-pass route with fp32 atomic dK (not bitwise reproducible)")
+    ap.add_argument("--dk-route", choices=("auto", "key_ranges", "slot_rows"), default="auto",
+                    help="deterministic dK route: by selection density (auto), or forced")
     ap.add_argument("--bf16-out", action="store_true",
                     help="d_q, d_w and d_k written as bf16 (the fp32 results rounded)")
     ap.add_argument("--forward", action="store_true",
@@ -97,7 +99,9 @@ def main():
         sys.exit(2)
     flags = (ibwd.IBWD_FLAG_DETERMINISTIC if args.deterministic else 0) | \
         (ibwd.IBWD_FLAG_ATOMIC_DK if args.atomic_dk else 0) | \
-        (ibwd.IBWD_FLAG_BF16_OUT if args.bf16_out else 0)
+        (ibwd.IBWD_FLAG_BF16_OUT if args.bf16_out else 0) | \
+        ({"auto": 0, "key_ranges": ibwd.IBWD_FLAG_DK_KEY_RANGES,
+          "slot_rows": ibwd.IBWD_FLAG_DK_SLOT_ROWS}[args.dk_route] if ids is not None else 0)
     ws_bytes = ibwd.indexer_bwd_workspace_bytes(wl.dense, B, S_q, S_k, H, D, wl.topk, flags)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.Stream(device=dev)
@@ -110,7 +114,8 @@ def main():
         else:
             ibwd.indexer_bwd_sparse(q, k, w, ids, I, p, dq, dw, dk,
                                     deterministic=args.deterministic, atomic_dk=args.atomic_dk,
-                                    bf16_out=args.bf16_out, workspace=ws, stream=stream)
+                                    bf16_out=args.bf16_out, dk_route=args.dk_route, workspace=ws,
+                                    stream=stream)
 
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib << 18  # fp32 elements
@@ -172,8 +177,9 @@ def main():
             per_kernel.setdefault((stage, name), []).append(prev.elapsed_time(e) * 1e3)
             prev = e
     kernels = []
+    slot_rows = any(name == "dk_rows_kernel" for (_, name) in per_kernel)
     for (stage, name), ts in sorted(per_kernel.items()):
-        bound, work = kernel_model(name, wl, B, H, D, S_q, S_k, 2 if args.bf16_out else 4)
+        bound, work = kernel_model(name, wl, B, H, D, S_q, S_k, 2 if args.bf16_out else 4, slot_rows)
         mean_k = statistics.fmean(ts)
         if bound == "mfma":
             ach, peak, unit = work / (mean_k * 1e-6) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
@@ -213,7 +219,8 @@ def main():
                    "topk": None if wl.dense else wl.topk, "pad_frac": wl.pad_frac,
                    "sorted_ids": wl.sorted_ids, "dense": wl.dense,
                    "deterministic": bool(args.deterministic), "atomic_dk": bool(args.atomic_dk),
-                   "bf16_out": bool(args.bf16_out)},
+                   "bf16_out": bool(args.bf16_out),
+                   "dk_route": "atomic" if args.atomic_dk else ("slot_rows" if slot_rows else "key_ranges")},
         "us_per_call_median": round(med_us, 2),
         "us_per_call_mean": round(mean_us, 2),
         "us_per_call_min": round(min(per_call_ms) * 1e3, 2),
@@ -477,34 +484,41 @@ def clocks_under_load(step, sync, samples=3, spacing=1.0):
             "max_mhz": vals[0].get("max_mhz")}
 
 
-def kernel_model(name, wl, B, H, D, S_q, S_k, out_bytes=4):
+def query_blocks(B, S_q, S_k):
+    """Query blocks as the library lays them out: 128-key ranges, about 512
+    range workgroups, at most 512 queries per block."""
+    nr = (S_k + 127) // 128
+    nqb = max(-(-512 // (nr * B)), -(-S_q // 512))
+    nqb = max(1, min(nqb, S_q))
+    qbs = -(-S_q // nqb)
+    return -(-S_q // qbs)
+
+
+def kernel_model(name, wl, B, H, D, S_q, S_k, out_bytes=4, slot_rows=False):
     """(bound, algorithmic work per launch) of one kernel of the call.
 
     Work units per query row are the row's slots (topk, or t+1 for the dense
     variant): the prep kernel reads the slot inputs and writes one 8-byte
     {position, dI} per slot, the row kernels do GEMM1 + GEMM2 (4*H*D FLOP per slot), the range
-    kernel the dK GEMM (2*H*D per slot), the atomic-route row kernel all three.
-    The slab sum reads every query block's partial dK once and writes d_k
-    (out_bytes per element)."""
+    kernel the dK GEMM (2*H*D per slot), the atomic-route row kernel all three, and
+    so does the row kernel of the slot-row route (its third product is the slot's
+    dK row).  The slot-row sum reads each slot's dK row and key once and writes
+    the query blocks' partial dK; the slab sum reads every query block's partial
+    dK once and writes d_k (out_bytes per element)."""
     slots = wl.flops() // (6 * H * D)
     if name == "row_prep_kernel":
         # ids (sparse), I and p read once, {position, dI} written per slot
         return "hbm", (16 if wl.dense else 20) * slots
     if name == "row_export_kernel":
-        return "mfma", 4 * H * D * slots
+        return "mfma", (6 if slot_rows else 4) * H * D * slots
     if name == "dk_range_kernel":
         return "mfma", 2 * H * D * slots
+    if name == "dk_rows_kernel":
+        return "hbm", (D * 4 + 4) * slots + query_blocks(B, S_q, S_k) * B * S_k * D * 4
     if name == "row_kernel":
         return "mfma", 6 * H * D * slots
     if name == "dk_sum_kernel":
-        # query blocks as the library lays them out: 128-key ranges, about
-        # 512 range workgroups, at most 512 queries per block
-        nr = (S_k + 127) // 128
-        nqb = max(-(-512 // (nr * B)), -(-S_q // 512))
-        nqb = max(1, min(nqb, S_q))
-        qbs = -(-S_q // nqb)
-        nqb = -(-S_q // qbs)
-        return "hbm", (nqb * 4 + out_bytes) * B * S_k * D
+        return "hbm", (query_blocks(B, S_q, S_k) * 4 + out_bytes) * B * S_k * D
     if name == "zero_u32_kernel":
         return "hbm", B * S_k * D * 4
     raise KeyError(name)

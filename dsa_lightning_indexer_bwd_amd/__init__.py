@@ -32,6 +32,8 @@ __all__ = [
     "IBWD_FLAG_ATOMIC_DK",
     "IBWD_FLAG_GLOBAL_IDS",
     "IBWD_FLAG_BF16_OUT",
+    "IBWD_FLAG_DK_KEY_RANGES",
+    "IBWD_FLAG_DK_SLOT_ROWS",
     "IndexerBwdError",
 ]
 
@@ -43,6 +45,9 @@ IBWD_FLAG_DETERMINISTIC = 1
 IBWD_FLAG_ATOMIC_DK = 2
 IBWD_FLAG_GLOBAL_IDS = 4
 IBWD_FLAG_BF16_OUT = 8
+IBWD_FLAG_DK_KEY_RANGES = 16
+IBWD_FLAG_DK_SLOT_ROWS = 32
+_DK_ROUTES = {"auto": 0, "key_ranges": IBWD_FLAG_DK_KEY_RANGES, "slot_rows": IBWD_FLAG_DK_SLOT_ROWS}
 IBWD_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_indexer_bwd.so")
@@ -196,21 +201,25 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
-def _flags(deterministic: bool, atomic_dk: bool, bf16_out: bool) -> int:
+def _flags(deterministic: bool, atomic_dk: bool, bf16_out: bool, dk_route: str = "auto") -> int:
+    if dk_route not in _DK_ROUTES:
+        raise ValueError("dk_route must be one of %s" % sorted(_DK_ROUTES))
     return ((IBWD_FLAG_DETERMINISTIC if deterministic else 0) | (IBWD_FLAG_ATOMIC_DK if atomic_dk else 0)
-            | (IBWD_FLAG_BF16_OUT if bf16_out else 0))
+            | (IBWD_FLAG_BF16_OUT if bf16_out else 0) | _DK_ROUTES[dk_route])
 
 
 def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w=None, d_k=None, *,
                        sm_scale: float = 1.0, grad_loss: float = 1.0, deterministic: bool = False,
                        atomic_dk: bool = False, global_ids: bool = False, bf16_out: bool = False,
-                       workspace=None, stream=None) -> Tuple:
+                       dk_route: str = "auto", workspace=None, stream=None) -> Tuple:
     """Backward of the top-k indexer.  Returns (d_q, d_w, d_k), all fp32, or all
     bf16 with bf16_out (the fp32 results rounded to nearest even; not with atomic_dk).
 
     q [B,S_q,H,D] bf16, k [B,S_k,D] bf16, w [B,S_q,H] fp32, topk_ids [B,S_q,topk]
     int32, index_score / attn_score [B,S_q,topk] fp32.  Outputs are overwritten.
     atomic_dk selects the single-pass fp32-atomic dK route (no workspace).
+    dk_route chooses between the deterministic routes: "auto" (by selection
+    density), "key_ranges" or "slot_rows".
     global_ids: the ids index the flattened [B*S_k] keys; a row of batch b keeps
     only ids in [b*S_k, (b+1)*S_k), every other id is padding.
     """
@@ -226,7 +235,7 @@ def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w
     _check(attn_score, torch.float32, (B, S_q, topk), "attn_score")
     s = _stream(stream, q.device)
     d_q, d_w, d_k = _outputs(q, k, d_q, d_w, d_k, bf16_out, s)
-    flags = _flags(deterministic, atomic_dk, bf16_out) | (IBWD_FLAG_GLOBAL_IDS if global_ids else 0)
+    flags = _flags(deterministic, atomic_dk, bf16_out, dk_route) | (IBWD_FLAG_GLOBAL_IDS if global_ids else 0)
     workspace, ws_bytes = _workspace(False, B, S_q, S_k, H, D, topk, flags, workspace, q.device, s)
     st = library().indexer_bwd_sparse(
         _ptr(q), _ptr(k), _ptr(w), _ptr(topk_ids), _ptr(index_score), _ptr(attn_score), _ptr(d_q),
@@ -240,7 +249,8 @@ def indexer_bwd_sparse(q, k, w, topk_ids, index_score, attn_score, d_q=None, d_w
 def indexer_bwd_sparse_noalloc(q, k, w, topk_ids, index_score, attn_score, d_q, d_w, d_k, *,
                                sm_scale: float = 1.0, grad_loss: float = 1.0,
                                deterministic: bool = False, atomic_dk: bool = False,
-                               global_ids: bool = False, bf16_out: bool = False, stream=None):
+                               global_ids: bool = False, bf16_out: bool = False,
+                               dk_route: str = "auto", stream=None):
     """indexer_bwd_sparse through the allocation-free entry point: the library's
     own per-GPU scratch array (IBWD_NOALLOC_SCRATCH_BYTES) instead of a workspace.
     The outputs must be given (nothing is allocated here); returns them."""
@@ -260,7 +270,7 @@ def indexer_bwd_sparse_noalloc(q, k, w, topk_ids, index_score, attn_score, d_q, 
     for t, shp, name in zip((d_q, d_w, d_k), ((B, S_q, H, D), (B, S_q, H), (B, S_k, D)),
                             ("d_q", "d_w", "d_k")):
         _check(t, dt, shp, name)
-    flags = _flags(deterministic, atomic_dk, bf16_out) | (IBWD_FLAG_GLOBAL_IDS if global_ids else 0)
+    flags = _flags(deterministic, atomic_dk, bf16_out, dk_route) | (IBWD_FLAG_GLOBAL_IDS if global_ids else 0)
     s = _stream(stream, q.device)
     st = library().indexer_bwd_sparse_noalloc(
         _ptr(q), _ptr(k), _ptr(w), _ptr(topk_ids), _ptr(index_score), _ptr(attn_score), _ptr(d_q),

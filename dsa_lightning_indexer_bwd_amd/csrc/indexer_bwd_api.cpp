@@ -56,9 +56,13 @@ int check_common(const void* q, const void* k, const float* w, const float* I, c
   if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, row_len))
     return IBWD_ERR_INVALID_ARGUMENT;
   if ((flags & ~(IBWD_FLAG_DETERMINISTIC | IBWD_FLAG_ATOMIC_DK | IBWD_FLAG_GLOBAL_IDS |
-                 IBWD_FLAG_BF16_OUT)) != 0)
+                 IBWD_FLAG_BF16_OUT | IBWD_FLAG_DK_KEY_RANGES | IBWD_FLAG_DK_SLOT_ROWS)) != 0)
     return IBWD_ERR_INVALID_ARGUMENT;
   if ((flags & IBWD_FLAG_DETERMINISTIC) && (flags & IBWD_FLAG_ATOMIC_DK)) return IBWD_ERR_INVALID_ARGUMENT;
+  // the route flags choose between the deterministic routes
+  if ((flags & IBWD_FLAG_DK_KEY_RANGES) && (flags & IBWD_FLAG_DK_SLOT_ROWS)) return IBWD_ERR_INVALID_ARGUMENT;
+  if ((flags & IBWD_FLAG_ATOMIC_DK) && (flags & (IBWD_FLAG_DK_KEY_RANGES | IBWD_FLAG_DK_SLOT_ROWS)))
+    return IBWD_ERR_INVALID_ARGUMENT;
   // the atomic route accumulates dK in d_k itself, which needs fp32
   if ((flags & IBWD_FLAG_BF16_OUT) && (flags & IBWD_FLAG_ATOMIC_DK)) return IBWD_ERR_INVALID_ARGUMENT;
   // the row kernel buckets a row's slots into at most kMaxRanges key ranges
@@ -71,10 +75,18 @@ int check_common(const void* q, const void* k, const float* w, const float* I, c
   return IBWD_OK;
 }
 
+int route_force(uint32_t flags) {
+  return (flags & IBWD_FLAG_DK_SLOT_ROWS) ? 2 : (flags & IBWD_FLAG_DK_KEY_RANGES) ? 1 : 0;
+}
+
+bool slot_rows(int64_t S_k, int64_t row_len, bool dense, uint32_t flags) {
+  return ibwd::use_slot_rows(S_k, row_len, dense, route_force(flags));
+}
+
 size_t workspace_bytes(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
-                       int64_t row_len, uint32_t flags) {
+                       int64_t row_len, bool dense, uint32_t flags) {
   if (flags & IBWD_FLAG_ATOMIC_DK) return 0;
-  return ibwd::make_layout(B, S_q, S_k, H, D, row_len).total;
+  return ibwd::make_layout(B, S_q, S_k, H, D, row_len, slot_rows(S_k, row_len, dense, flags)).total;
 }
 
 // Both sparse entry points: every check first, then the launch.  noalloc: the
@@ -89,7 +101,7 @@ int sparse_call(const void* q, const void* k, const float* w, const int32_t* top
   if (st != IBWD_OK) return st;
   if (!topk_ids || !aligned(topk_ids, 4)) return IBWD_ERR_INVALID_ARGUMENT;
   if (topk > S_k) return IBWD_ERR_INVALID_ARGUMENT;  // more slots than keys
-  const size_t need = workspace_bytes(B, S_q, S_k, H, D, topk, flags);
+  const size_t need = workspace_bytes(B, S_q, S_k, H, D, topk, false, flags);
   if (noalloc) {
     if (need > ibwd::kNoAllocScratchBytes) return IBWD_ERR_INVALID_ARGUMENT;
   } else if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256))) {
@@ -121,7 +133,9 @@ int sparse_call(const void* q, const void* k, const float* w, const int32_t* top
   P.q_offset = 0;
   P.sm_scale = sm_scale;
   P.grad_loss = grad_loss;
-  P.route = (flags & IBWD_FLAG_ATOMIC_DK) ? ibwd::kDkAtomic : ibwd::kDkTwoPass;
+  P.route = (flags & IBWD_FLAG_ATOMIC_DK)         ? ibwd::kDkAtomic
+            : slot_rows(S_k, topk, false, flags) ? ibwd::kDkSlotRows
+                                                 : ibwd::kDkTwoPass;
   return ibwd::launch(P, workspace, stream) == hipSuccess ? IBWD_OK : IBWD_ERR_HIP;
 }
 
@@ -159,7 +173,8 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
   if (q_offset < -(int64_t(1) << 40) || q_offset > (int64_t(1) << 40))
     return IBWD_ERR_INVALID_ARGUMENT;
   if (flags & IBWD_FLAG_GLOBAL_IDS) return IBWD_ERR_INVALID_ARGUMENT;  // the dense call has no ids
-  size_t need = workspace_bytes(B, S_q, S_k, H, D, S_k, flags);
+  if (flags & IBWD_FLAG_DK_SLOT_ROWS) return IBWD_ERR_INVALID_ARGUMENT;  // every key selected
+  size_t need = workspace_bytes(B, S_q, S_k, H, D, S_k, true, flags);
   if (need > 0 && (ws_bytes < need || !workspace || !aligned(workspace, 256)))
     return IBWD_ERR_INVALID_ARGUMENT;
   st = device_status();
@@ -197,7 +212,8 @@ size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_
   if (row_len > S_k) return 0;
   if (D != 32 && D != 64 && D != 128) return 0;
   if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, row_len)) return 0;
-  return workspace_bytes(B, S_q, S_k, H, D, row_len, flags);
+  if (dense && (flags & IBWD_FLAG_DK_SLOT_ROWS)) return 0;
+  return workspace_bytes(B, S_q, S_k, H, D, row_len, dense != 0, flags);
 }
 
 int indexer_fwd_scores(const void* q, const void* k, const float* w, float* scores, int64_t B,

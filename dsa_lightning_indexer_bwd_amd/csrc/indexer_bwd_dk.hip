@@ -583,6 +583,164 @@ __global__ __launch_bounds__(256) void dk_sum_kernel(Problem P) {
   }
 }
 
+// Slot-row route: one wave per (32-key block of a key range, query block,
+// batch).  The row kernel left, for every valid slot, its key and its dK row
+// C = dI * sum_h [S > 0] (w*q) in bf16 at its record position (the prep kernel
+// groups a row's records by key range, slot order within a range).  The wave
+// walks the query block's queries in order, 64 at a time: their {first, end}
+// of this range give a run of records per query, numbered across the 64
+// queries by a prefix sum; each lane takes one record of the run (its query by
+// a binary search over the run starts), reads its key, and a ballot picks the
+// records of the wave's 32 keys.  Keys are read 256 records at a time, the
+// picked records queued in LDS, and their rows read 16 at a time with the next
+// 16 in flight, and added in fp32, in (query, position) order, into the wave's
+// 32 x D partial dK, which it holds in registers (lane l: columns
+// E*l .. E*l+E-1 of every key; the key, uniform over the wave, indexes the
+// registers).  The order is fixed, so the result does not depend on
+// scheduling.  The partial dK then goes to the query block's slab.
+constexpr int kRowBlocks = 16;               // key blocks per range in the slot-row sum
+constexpr int KW = kRangeKeys / kRowBlocks;  // keys per wave
+template <int D>
+__global__ __launch_bounds__(64) void dk_rows_kernel(Problem P) {
+  constexpr int E = D >= 128 ? 2 : 1;  // bf16 of a row per lane
+  constexpr int NL = D / E;            // lanes covering a row (32 at D = 32)
+  constexpr int kBatch = 16;           // row reads per batch (two batches in flight)
+  constexpr int kPiece = 4;            // 64-record chunks whose keys are read together
+  __shared__ int ex_s[64], base_s[64];
+  __shared__ int2 queue[kPiece * 64];  // selected {record, key - k0} of a piece
+  const int lane = threadIdx.x;
+  const int lc = lane < NL ? lane : 0;
+  const int blk = int(blockIdx.x) % kRowBlocks;
+  const int rg = int(blockIdx.x) / kRowBlocks;
+  const int qb = int(blockIdx.y);
+  const int64_t b = blockIdx.z;
+  const int k0 = rg * kRangeKeys + KW * blk;
+  // acc0[k], acc1[k]: this lane's columns E*lane, E*lane + 1 of key k0 + k
+  typedef float f32xkw_t __attribute__((ext_vector_type(KW)));
+  f32xkw_t acc0 = f32xkw_t{}, acc1 = f32xkw_t{};
+  const int64_t t0 = int64_t(qb) * P.QBS;
+  const int64_t t1 = t0 + P.QBS < P.S_q ? t0 + P.QBS : P.S_q;
+  const int2* offs = reinterpret_cast<const int2*>(P.offs);
+  auto load_fe = [&](int64_t tb) -> int2 {
+    const int64_t t = tb + lane;
+    return t < t1 ? offs[(b * P.S_q + t) * P.NR + rg] : make_int2(0, 0);
+  };
+  // record f of the current run: its global record index (or 0) and key (or -1)
+  auto locate = [&](int f, int T, int& rec) -> int {
+    int lo = 0;
+#pragma unroll
+    for (int st = 32; st > 0; st >>= 1)
+      if (ex_s[lo + st] <= f) lo += st;  // a query without records shares its start with the next
+    rec = f < T ? base_s[lo] + (f - ex_s[lo]) : 0;
+    return f < T ? P.skey[rec] : -1;
+  };
+  auto row_at = [&](int rec) -> uint32_t {
+    const uint16_t* src = P.crow + int64_t(rec) * D + E * lc;
+    return E == 2 ? *reinterpret_cast<const uint32_t*>(src) : uint32_t(*src);
+  };
+  // acc[kl] += row; kl is uniform over the wave, so the indexed register
+  // update needs no per-lane selection (-1: nothing)
+  auto add_row = [&](int kl, uint32_t v) {
+    if (kl >= 0) {
+      acc0[kl] += E == 2 ? bf16_lo(v) : __uint_as_float(v << 16);
+      if (E == 2) acc1[kl] += bf16_hi(v);
+    }
+  };
+  int2 fe = load_fe(t0);
+  for (int64_t tb = t0; tb < t1; tb += 64) {
+    const int n = fe.y - fe.x;
+    int incl = n;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const int T = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+    const int64_t t = tb + lane;
+    wave_lds_sync();  // the previous batch's searches are done
+    ex_s[lane] = incl - n;
+    base_s[lane] = t < t1 ? int((b * P.S_q + t) * P.rec_stride) + fe.x : 0;
+    wave_lds_sync();
+    fe = load_fe(tb + 64);  // the next batch's runs
+    for (int p0 = 0; p0 < T; p0 += 64 * kPiece) {
+      // the keys of kPiece x 64 records, their reads in flight together
+      int recs[kPiece], keys[kPiece];
+#pragma unroll
+      for (int c = 0; c < kPiece; ++c) keys[c] = locate(p0 + 64 * c + lane, T, recs[c]);
+      // the records of the wave's keys, in record order, into the queue
+      int qn = 0;
+#pragma unroll
+      for (int c = 0; c < kPiece; ++c) {
+        const int loc = keys[c] - k0;
+        const bool sel = unsigned(loc) < unsigned(KW);
+        const uint64_t m = ballot(sel);
+        if (sel) queue[qn + __popcll(m & lanemask_lt())] = make_int2(recs[c], loc);
+        qn += __popcll(m);
+      }
+      wave_lds_sync();
+      if (qn > 0) {
+        // rows kBatch at a time; the next kBatch are read while the current
+        // ones are added.  Every read is issued (entries past the queue read
+        // record 0 and add nothing), so the compiler's wait before each add
+        // covers only the reads issued before it.
+        uint32_t va[kBatch], vb[kBatch];
+        int la[kBatch], lb[kBatch];
+        auto fetch = [&](int q0, uint32_t(&v)[kBatch], int(&l)[kBatch]) {
+          const int qi = q0 + (lane & (kBatch - 1));
+          const int2 e = qi < qn ? queue[qi] : make_int2(0, -1);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            l[u] = __builtin_amdgcn_readlane(e.y, u);
+            v[u] = row_at(__builtin_amdgcn_readlane(e.x, u));
+          }
+        };
+        fetch(0, va, la);
+        for (int q0 = 0; q0 < qn; q0 += 2 * kBatch) {
+          fetch(q0 + kBatch, vb, lb);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) add_row(la[u], va[u]);
+          fetch(q0 + 2 * kBatch, va, la);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) add_row(lb[u], vb[u]);
+        }
+      }
+      wave_lds_sync();  // the queue is read before the next piece fills it
+    }
+  }
+  float* dst = P.slab + ((b * P.NQB + qb) * (P.NR * kRangeKeys) + k0) * D;
+  if (lane < NL) {
+#pragma unroll
+    for (int k = 0; k < KW; ++k) {
+      if (k0 + k < P.S_k) {
+        if (E == 2)
+          *reinterpret_cast<float2*>(dst + k * D + 2 * lane) = make_float2(acc0[k], acc1[k]);
+        else
+          dst[k * D + lane] = acc0[k];
+      }
+    }
+  }
+}
+
+hipError_t launch_sum(const Problem& P, hipStream_t stream) {
+  const int64_t n4 = P.B * P.S_k * P.D / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  dk_sum_kernel<<<unsigned(blocks), 256, 0, stream>>>(P);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  stage_done(3, "dk_sum_kernel");
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_rows_t(const Problem& P, hipStream_t stream) {
+  const dim3 grid(unsigned(P.NR * kRowBlocks), unsigned(P.NQB), unsigned(P.B));
+  dk_rows_kernel<D><<<grid, 64, 0, stream>>>(P);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  stage_done(2, "dk_rows_kernel");
+  return launch_sum(P, stream);
+}
+
 template <int NH, int D, bool SKIP>
 hipError_t launch_range(const Problem& P, hipStream_t stream) {
   using S = DkShape<D, NH * 32>;
@@ -601,16 +759,23 @@ hipError_t launch_dk_t(const Problem& P, hipStream_t stream) {
   hipError_t err = skip ? launch_range<NH, D, true>(P, stream) : launch_range<NH, D, false>(P, stream);
   if (err != hipSuccess) return err;
   stage_done(2, "dk_range_kernel");
-  const int64_t n4 = P.B * P.S_k * P.D / 4;
-  int64_t blocks = (n4 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  dk_sum_kernel<<<unsigned(blocks), 256, 0, stream>>>(P);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  stage_done(3, "dk_sum_kernel");
-  return hipSuccess;
+  return launch_sum(P, stream);
 }
 
 }  // namespace
+
+hipError_t launch_dk_rows(const Problem& P, hipStream_t stream) {
+  switch (P.D) {
+    case 32:
+      return launch_rows_t<32>(P, stream);
+    case 64:
+      return launch_rows_t<64>(P, stream);
+    case 128:
+      return launch_rows_t<128>(P, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_dk(const Problem& P, hipStream_t stream) {
   const bool two = P.H > 32;

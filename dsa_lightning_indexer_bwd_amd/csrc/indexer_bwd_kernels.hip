@@ -7,6 +7,13 @@
 //                     (key, dI, sign mask of S over h), (w*q)^T
 //     dk_range_kernel one workgroup per (key range, query block): dK slabs in LDS
 //     dk_sum_kernel   d_k = fixed-order sum of the query-block slabs
+//   slot-row route (deterministic, for rows that select few keys per range):
+//     row_prep_kernel   as above, ranges packed without alignment
+//     row_export_kernel dQ, dW, and per valid slot its key and its dK row
+//                       C = dI * sum_h [S>0] (w*q) (an MFMA product per chunk)
+//     dk_rows_kernel    one wave per (32 keys, query block): the rows of its
+//                       keys added in LDS in record order, into the slabs
+//     dk_sum_kernel     as above
 //   atomic route:
 //     fill d_k with zeros, then row_kernel with fp32 atomic dK scatter
 #include <hip/hip_runtime.h>
@@ -70,7 +77,7 @@ void stage_done(int stage, const char* kernel) {
 
 hipError_t launch(Problem P, void* workspace, hipStream_t stream) {
   hipError_t err;
-  const Layout L = make_layout(P.B, P.S_q, P.S_k, P.H, P.D, P.row_len);
+  const Layout L = make_layout(P.B, P.S_q, P.S_k, P.H, P.D, P.row_len, P.route == kDkSlotRows);
   P.rec_stride = L.rec_stride;
   P.RK = L.RK;
   P.NR = L.NR;
@@ -88,6 +95,15 @@ hipError_t launch(Problem P, void* workspace, hipStream_t stream) {
     return hipSuccess;
   }
   char* ws = static_cast<char*>(workspace);
+  if (P.route == kDkSlotRows) {
+    P.offs = reinterpret_cast<int*>(ws + L.off_offs);
+    P.slot = reinterpret_cast<int*>(ws + L.off_slot);
+    P.skey = reinterpret_cast<int*>(ws + L.off_skey);
+    P.crow = reinterpret_cast<uint16_t*>(ws + L.off_crow);
+    P.slab = reinterpret_cast<float*>(ws + L.off_slab);
+    if ((err = launch_rows_export(P, stream)) != hipSuccess) return err;  // stages 0, 1
+    return launch_dk_rows(P, stream);  // stages 2, 3
+  }
   P.rkd = reinterpret_cast<int*>(ws + L.off_rkd);
   P.rmask = reinterpret_cast<uint32_t*>(ws + L.off_rmask);
   P.offs = reinterpret_cast<int*>(ws + L.off_offs);

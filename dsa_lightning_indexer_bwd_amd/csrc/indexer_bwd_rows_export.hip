@@ -10,7 +10,11 @@
 //   dQ[t,h,:] = w[t,h] * sum_j G'[h,j] * k[id_j,:]
 // and, for the range kernel that finishes dK, per valid slot a record
 // {key, dI, the sign bits [S[h,j] > 0] of every h} grouped by key range, and
-// (w*q)^T of the row.
+// (w*q)^T of the row.  For the slot-row route the kernel instead writes, per
+// valid slot, its key and its dK row
+//   C[j,:] = sum_h G'[h,j] (w*q)[h,:] = dI_j * sum_h [S[h,j] > 0] (w*q)[h,:]
+// computed on the matrix cores from the same sign bits and rounded to bf16
+// (see crow_pass).
 //
 // The 64 heads are split over the two waves of a workgroup (one row per
 // workgroup).  Each wave then needs half the registers (dQ' accumulators, Q,
@@ -97,6 +101,28 @@ struct ExportLds {
   static constexpr int kBytes = kW1Off + kW1Ring * kSlots * 4;
 };
 
+// LDS of the slot-row variant (CROWS): the row kernel's layout, then wave 0's
+// sign words (a ring like wave 1's) and (w*q)^T of the row, [D][HP] bf16, kept
+// for the whole row as the A operand of C^T.
+template <int D, int NG, bool CROWS>
+struct RowLds {
+  using L = ExportLds<D>;
+  static constexpr int HP = 32 * NG;
+  static constexpr int kW0Off = L::kBytes;
+  static constexpr int kQtOff = kW0Off + (CROWS ? kW1Ring * kSlots * 4 : 0);
+  static constexpr int kQtPitch = HP * 2;
+  static constexpr int kBytes = kQtOff + (CROWS ? D * kQtPitch : 0);
+  static_assert(L::kBytes % 16 == 0, "16-byte aligned Q' rows");
+  // byte offset of 16-byte chunk c (heads 8c .. 8c+7) of row d: chunks XORed by
+  // the row's place within its 256-byte line, so that 16 consecutive rows at
+  // one chunk (the A-operand reads) fall on distinct banks
+  __device__ static int qt_at(int d, int c) {
+    constexpr int rpb = 256 / kQtPitch;  // rows per 256 bytes
+    constexpr int cpr = kQtPitch / 16;   // chunks per row
+    return d * kQtPitch + ((c ^ ((d / rpb) & (cpr - 1))) << 4);
+  }
+};
+
 struct Raw {
   int id;
   int2 pd;  // {record position (-1: padding), dI bits} from the prep kernel
@@ -127,7 +153,8 @@ __device__ __forceinline__ uint64_t same_range_lanes(bool valid, int r, int nbit
 //   scan:   range starts; {first, end} of every range to `offs`
 //   pass 2: positions (range start + earlier slots of the range, from the
 //           same ballots) and dI, as {position or -1, dI} per slot
-template <bool DENSE>
+// PACKED (slot-row route): ranges follow each other without alignment.
+template <bool DENSE, bool PACKED>
 __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
   extern __shared__ int cursor[];  // one int per key range
   const int lane = threadIdx.x;
@@ -186,7 +213,7 @@ __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
     const int s0 = lane * per < NR ? lane * per : NR;
     const int s1 = s0 + per < NR ? s0 + per : NR;
     int sum = 0;
-    for (int i = s0; i < s1; ++i) sum += (cursor[i] + 3) & ~3;
+    for (int i = s0; i < s1; ++i) sum += PACKED ? cursor[i] : (cursor[i] + 3) & ~3;
     int incl = sum;
     for (int o = 1; o < 64; o <<= 1) {
       const int v = __shfl_up(incl, o, 64);
@@ -198,7 +225,7 @@ __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
       const int cnt = cursor[i];
       cursor[i] = run;
       offrow[i] = make_int2(run, run + cnt);
-      run += (cnt + 3) & ~3;
+      run += PACKED ? cnt : (cnt + 3) & ~3;
     }
     lds_order();
   }
@@ -242,12 +269,16 @@ __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
 // SPLIT: GEMM2 takes G' as two bf16 terms, bf16(G') and bf16(G' - bf16(G')),
 // so that dQ carries only fp32 accumulation error (for bf16 outputs, whose own
 // rounding would otherwise add to that of G').
-template <int D, bool DENSE, int NG, bool SPLIT>
+// CROWS: the slot-row route's outputs (keys and dK rows) instead of records and
+// (w*q)^T.
+template <int D, bool DENSE, int NG, bool SPLIT, bool CROWS>
 __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) void row_export_kernel(
     Problem P) {
   constexpr int KD = D / 16;  // GEMM1 k-steps over d
   constexpr int ND = D / 32;  // GEMM2 32-wide d tiles
   using L = ExportLds<D>;
+  using RL = RowLds<D, NG, CROWS>;
+  static_assert(!(CROWS && DENSE), "the dense call keeps the key-range route");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int lane = threadIdx.x & 63;
@@ -329,8 +360,11 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int r0 = 16 * ks + 8 * half;
-        *reinterpret_cast<u32x4_t*>(qtrow + (32 * nd + l32) * HP + r0) =
-            L::tr8(qs, r0, r0 + 4, col0);
+        const u32x4_t v = L::tr8(qs, r0, r0 + 4, col0);
+        if (CROWS)  // row d, heads 32g + r0 .. +7: chunk 4g + 2ks + half
+          *reinterpret_cast<u32x4_t*>(lds + RL::kQtOff + RL::qt_at(32 * nd + l32, 4 * g + 2 * ks + half)) = v;
+        else
+          *reinterpret_cast<u32x4_t*>(qtrow + (32 * nd + l32) * HP + r0) = v;
       }
     }
     __syncthreads();  // both Q' tiles read before the K tiles take their place
@@ -350,6 +384,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     return lds + L::kStageOff + (c & (kRowStages - 1)) * L::kStageBytes;
   };
   uint32_t* w1x = reinterpret_cast<uint32_t*>(lds + L::kW1Off);
+  uint32_t* w0x = reinterpret_cast<uint32_t*>(lds + RL::kW0Off);  // CROWS only
   // key of the lane's slot; the dI wave also publishes dI and key, the record
   // wave the position of the slot's record (lanes l and l+32 write the same
   // values)
@@ -363,7 +398,9 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
       // the part of dI that bf16(dI) drops (exact in fp32)
       if (SPLIT) reinterpret_cast<float*>(stage_ptr(c) + kSlots * 12)[l32] = dI - bf16_lo(pack_bf16(dI, 0.f));
     }
-    if (rec_wave) reinterpret_cast<int*>(stage_ptr(c) + kSlots * 8)[l32] = v.pd.x;
+    // slots past the row (j >= row_len) load a clamped copy of the last slot's
+    // entry: their position is -1 like that of every other padding slot
+    if (rec_wave) reinterpret_cast<int*>(stage_ptr(c) + kSlots * 8)[l32] = key >= 0 ? v.pd.x : -1;
     return key;
   };
   // Each wave gathers only its RW rows of a chunk's K tile (all 32 when it is
@@ -419,9 +456,97 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   uint32_t prev_mask = 0u;
   auto store_records = [&](int c_prev) {
     if (rec_wave && prev_valid && prev_pos >= 0) {
-      const uint32_t w1 = NG == 2 ? w1x[(c_prev & (kW1Ring - 1)) * kSlots + l32] : 0u;
-      rkd[prev_pos] = prev_kd;
-      rmask[prev_pos] = make_uint2(prev_mask, w1);
+      if (CROWS) {
+        P.skey[r * P.rec_stride + prev_pos] = prev_kd.x;
+      } else {
+        const uint32_t w1 = NG == 2 ? w1x[(c_prev & (kW1Ring - 1)) * kSlots + l32] : 0u;
+        rkd[prev_pos] = prev_kd;
+        rmask[prev_pos] = make_uint2(prev_mask, w1);
+      }
+    }
+  };
+
+  // ---- slot-row route: C^T[d][j] = sum_h (w*q)^T[d][h] G'[h][j] of chunk cc --
+  // M = d (the wave's 32-column blocks: wave g takes a contiguous half of D,
+  // at D = 32 wave 0 takes it all), N = slot j, K = heads.  The A operand
+  // (lane: row d, heads 16ks + 8half .. +7) is read from the LDS copy of
+  // (w*q)^T; the B operand (lane: slot l32, the same eight heads) is expanded
+  // from the slot's two sign words: head 16ks + 8half + e is bit
+  // 8(ks&1) + 4half + e/2 + 16(e&1) of word ks/2 (bit b of word g is head
+  // 32g + rotl5(b)), so a pair of heads is one shift, one AND and one 24-bit
+  // multiply by bf16(dI).  Lane (slot l32, half) then holds C[l32][d] for
+  // d = 32mb + 8i + 4half + 0..3, rounded to bf16 (nearest even).  For D >= 64
+  // the wave stages its columns of the 32 rows in LDS, in the rows of the K
+  // tile of chunk cc+2 that it gathers itself (free until it writes them later
+  // in the iteration), and stores each row's piece as contiguous 16-byte lanes;
+  // at D = 32 each lane stores its 8-byte pieces directly.  Padding slots
+  // (position -1, dI 0) write the row after the last record.
+  constexpr int MBT = D / 32;                                     // 32-column blocks
+  constexpr int MPW = NG == 1 ? MBT : (MBT >= 2 ? MBT / 2 : 1);  // blocks per wave
+  constexpr int SP = MPW * 64;                                    // staged row pitch, bytes
+  constexpr int SCPR = SP / 16;                                   // 16-byte chunks per staged row
+  constexpr int SRPB = SP >= 256 ? 1 : 256 / SP;                  // staged rows per 256 bytes
+  static_assert(D < 64 || 32 * SP <= (kSlots / NG) * L::kPitch, "staging fits the wave's rows of a K tile");
+  auto stg_at = [](int row, int ch) { return row * SP + ((ch ^ ((row / SRPB) & (SCPR - 1))) << 4); };
+  auto crow_pass = [&](int cc) {
+    const int mlo = NG == 1 ? 0 : g * MPW;  // first block of this wave
+    if (mlo >= MBT) return;                 // wave 1 at D = 32
+    const unsigned char* st = stage_ptr(cc);
+    const float dIj = reinterpret_cast<const float*>(st)[l32];
+    const uint32_t dib = pack_bf16(dIj, 0.f) & 0xffffu;
+    const uint32_t wd0 = w0x[(cc & (kW1Ring - 1)) * kSlots + l32];
+    const uint32_t wd1 = NG == 2 ? w1x[(cc & (kW1Ring - 1)) * kSlots + l32] : 0u;
+    const unsigned char* qtl = lds + RL::kQtOff;
+    unsigned char* stg = ktile(cc + 2) + (NG == 2 ? RW * g * L::kPitch : 0);
+    auto rec_of = [&](int pos) -> int64_t {
+      return pos >= 0 ? r * P.rec_stride + pos : P.B * P.S_q * P.rec_stride;
+    };
+#pragma unroll
+    for (int kp = 0; kp < MPW; kp += 2) {
+      const bool two = kp + 1 < MPW;
+      const int mb0 = mlo + kp;
+      f32x16_t ca = f32x16_t{}, cb = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < 2 * NG; ++ks) {
+        const uint32_t word = (ks < 2 ? wd0 : wd1) >> (8 * (ks & 1) + 4 * half);
+        u32x4_t bx;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bx[j] = __umul24((word >> j) & 0x10001u, dib);
+        const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(qtl + RL::qt_at(32 * mb0 + l32, 2 * ks + half));
+        ca = mfma32(a0, bx, ca);
+        if (two) {
+          const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(qtl + RL::qt_at(32 * mb0 + 32 + l32, 2 * ks + half));
+          cb = mfma32(a1, bx, cb);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint2 va = make_uint2(pack_bf16(ca[4 * i], ca[4 * i + 1]), pack_bf16(ca[4 * i + 2], ca[4 * i + 3]));
+        const uint2 vb = make_uint2(pack_bf16(cb[4 * i], cb[4 * i + 1]), pack_bf16(cb[4 * i + 2], cb[4 * i + 3]));
+        if (D >= 64) {
+          // local column 32k + 8i + 4half: 16-byte chunk 4k + i, bytes 8half..
+          *reinterpret_cast<uint2*>(stg + stg_at(l32, 4 * kp + i) + 8 * half) = va;
+          if (two) *reinterpret_cast<uint2*>(stg + stg_at(l32, 4 * kp + 4 + i) + 8 * half) = vb;
+        } else {
+          const int pos = reinterpret_cast<const int*>(st + kSlots * 8)[l32];
+          uint16_t* dst = P.crow + rec_of(pos) * D;
+          *reinterpret_cast<uint2*>(dst + 32 * mb0 + 8 * i + 4 * half) = va;
+          if (two) *reinterpret_cast<uint2*>(dst + 32 * mb0 + 32 + 8 * i + 4 * half) = vb;
+        }
+      }
+    }
+    if (D >= 64) {
+      wave_lds_sync();
+      constexpr int kRowsPer = 64 / SCPR;  // staged rows per 16-byte-lane pass
+#pragma unroll
+      for (int it = 0; it < kSlots / kRowsPer; ++it) {
+        const int row = it * kRowsPer + lane / SCPR;
+        const int ch = lane % SCPR;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg_at(row, ch));
+        const int pos = reinterpret_cast<const int*>(st + kSlots * 8)[row];
+        *reinterpret_cast<u32x4_t*>(P.crow + rec_of(pos) * D + 32 * mlo + 8 * ch) = v;
+      }
+      wave_lds_sync();  // staging read before the wave's K rows take its place
     }
   };
 
@@ -438,6 +563,9 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   // into its tile, gathers of chunk c+2
   auto step = [&](int c) {
     __syncthreads();  // K tile and stage of chunk c complete; chunk c-1 done by both waves
+    // chunk c-1's dK rows: both waves' sign words are visible now, and the
+    // stores go out before this iteration's loads
+    if (CROWS && c > 0) crow_pass(c - 1);
     // raised priority while this wave issues its MFMAs, so that the other wave
     // of the SIMD fills the gaps with its VALU work
     __builtin_amdgcn_s_setprio(1);
@@ -495,6 +623,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     }
     if (NG == 2 && g == 1 && lane < kSlots) w1x[(c & (kW1Ring - 1)) * kSlots + lane] = maskword;
+    if (CROWS && g == 0 && lane < kSlots) w0x[(c & (kW1Ring - 1)) * kSlots + lane] = maskword;
 
     // ---- GEMM2: dQ'[h][d] += G'[h][j] K[j][d] ----------------------------------
     // k-step ks covers slots 16*ks + {0..15}; register e of lane (half) is slot
@@ -527,6 +656,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
   for (int c = 0; c < nchunks; ++c) step(c);
   __syncthreads();  // the last chunk's sign words of wave 1
+  if (CROWS && nchunks > 0) crow_pass(nchunks - 1);
   store_records(nchunks - 1);
 
   // ---- row epilogue: dQ = w * dQ', dW -----------------------------------------
@@ -558,26 +688,29 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     epilogue(P.dq, P.dw, [](float v) { return v; });
 }
 
-template <int D, bool DENSE>
+template <int D, bool DENSE, int NG, bool CROWS>
+void launch_export(const Problem& P, hipStream_t stream) {
+  const dim3 grid(unsigned(P.B * P.S_q));
+  constexpr int kLds = RowLds<D, NG, CROWS>::kBytes;
+  // bf16 outputs take G' in two bf16 terms (the dQ rounding then stays the
+  // only one of note); fp32 outputs keep one
+  if (P.bf16_out)
+    row_export_kernel<D, DENSE, NG, true, CROWS><<<grid, 64 * NG, kLds, stream>>>(P);
+  else
+    row_export_kernel<D, DENSE, NG, false, CROWS><<<grid, 64 * NG, kLds, stream>>>(P);
+}
+
+template <int D, bool DENSE, bool CROWS>
 hipError_t launch_t(const Problem& P, hipStream_t stream) {
   const dim3 grid(unsigned(P.B * P.S_q));
-  row_prep_kernel<DENSE><<<grid, 64, size_t(P.NR) * 4, stream>>>(P);
+  row_prep_kernel<DENSE, CROWS><<<grid, 64, size_t(P.NR) * 4, stream>>>(P);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   stage_done(0, "row_prep_kernel");
-  // bf16 outputs take G' in two bf16 terms (the dQ rounding then stays the
-  // only one of note); fp32 outputs keep one
-  if (P.HP > 32) {
-    if (P.bf16_out)
-      row_export_kernel<D, DENSE, 2, true><<<grid, 128, ExportLds<D>::kBytes, stream>>>(P);
-    else
-      row_export_kernel<D, DENSE, 2, false><<<grid, 128, ExportLds<D>::kBytes, stream>>>(P);
-  } else {
-    if (P.bf16_out)
-      row_export_kernel<D, DENSE, 1, true><<<grid, 64, ExportLds<D>::kBytes, stream>>>(P);
-    else
-      row_export_kernel<D, DENSE, 1, false><<<grid, 64, ExportLds<D>::kBytes, stream>>>(P);
-  }
+  if (P.HP > 32)
+    launch_export<D, DENSE, 2, CROWS>(P, stream);
+  else
+    launch_export<D, DENSE, 1, CROWS>(P, stream);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   stage_done(1, "row_export_kernel");
   return hipSuccess;
@@ -585,7 +718,8 @@ hipError_t launch_t(const Problem& P, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const Problem& P, hipStream_t stream) {
-  return P.dense ? launch_t<D, true>(P, stream) : launch_t<D, false>(P, stream);
+  if (P.dense) return launch_t<D, true, false>(P, stream);
+  return P.route == kDkSlotRows ? launch_t<D, false, true>(P, stream) : launch_t<D, false, false>(P, stream);
 }
 
 }  // namespace

@@ -18,12 +18,25 @@ constexpr int kRecBlock = 128;       // records the range kernel stages per DMA
 enum DkRoute : int {
   kDkTwoPass = 0,  // masks + records exported, range-major LDS reduction (deterministic)
   kDkAtomic = 1,   // fp32 global atomics straight from the row kernel
+  kDkSlotRows = 2,  // per-slot dK rows from the row kernel, summed per key range (deterministic)
 };
+
+// Route of a deterministic call.  The key-range GEMM multiplies, per query and
+// 128-key range, every key of the range whether selected or not, and copies the
+// query's (w*q)^T into the range's workgroup: its cost follows (queries x
+// ranges).  Per-slot dK rows cost one fp32 row of D per selected slot, written
+// and read once: they win when a row selects few keys per range.
+// force: 0 = by density, 1 = key ranges, 2 = slot rows.
+inline bool use_slot_rows(int64_t S_k, int64_t row_len, bool dense, int force) {
+  if (dense) return false;
+  if (force) return force == 2;
+  return row_len * 16 <= S_k;
+}
 
 // Workspace layout of the two-pass dK route.  A row's valid slots are stored
 // as records grouped by key range (range r = key / RK), slot order within a
 // range; range r occupies [first_r, end_r), and every range starts at a
-// multiple of 4 entries.
+// multiple of 4 entries (key-range route; the slot-row route packs the ranges).
 //   rkd   [rows][rec_stride] int2   {key, dI bits} of the record
 //   rmask [rows][rec_stride][2] u32 sign bits [S > 0] of heads 0..31, 32..63
 //         (bit b of word g is head 32g + rotl5(b), rotl5 = 5-bit rotate left)
@@ -34,22 +47,29 @@ enum DkRoute : int {
 //   slab  [B][NQB][NR*RK][D] fp32   per query block partial dK
 // rec_stride = row_len + 3*NR (alignment of the ranges), rounded up to a
 // multiple of 4.
+// The slot-row route keeps offs, slot and slab, and replaces rkd, rmask and qt by
+//   skey  [rows][row_len] int        key of the record at each position
+//   crow  [rows][row_len][D] bf16    the slot's dK row C = dI * sum_h [S>0] (w*q)
+//         plus one row that padding slots write and nothing reads
+// with rec_stride = row_len (ranges packed without alignment).
 struct Layout {
   int64_t rows, row_len, rec_stride, HP, RK, NR, NQB, QBS, nchunk;
-  size_t off_rkd, off_rmask, off_offs, off_slot, off_qt, off_slab, total;
+  bool slot_rows;
+  size_t off_rkd, off_rmask, off_offs, off_slot, off_qt, off_slab, off_skey, off_crow, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
-                          int64_t row_len) {
+                          int64_t row_len, bool slot_rows) {
   Layout L{};
   L.rows = B * S_q;
   L.row_len = row_len;
+  L.slot_rows = slot_rows;
   L.HP = H > 32 ? 64 : 32;
   L.RK = kRangeKeys;
   L.NR = (S_k + L.RK - 1) / L.RK;
-  L.rec_stride = (row_len + 3 * L.NR + 3) & ~int64_t(3);  // 16-byte aligned rows
+  L.rec_stride = slot_rows ? row_len : (row_len + 3 * L.NR + 3) & ~int64_t(3);  // 16-byte aligned rows
   // about 512 range-kernel workgroups (two per CU), at most kMaxQueryBlock
   // queries each
   int64_t nqb = (512 + L.NR * B - 1) / (L.NR * B);
@@ -60,9 +80,23 @@ inline Layout make_layout(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_
   L.NQB = (S_q + L.QBS - 1) / L.QBS;
   L.nchunk = (row_len + kSlots - 1) / kSlots;
   const size_t recs = size_t(L.rows) * size_t(L.rec_stride);
+  size_t o = 0;
+  if (slot_rows) {
+    L.off_offs = o;
+    o = align256(o + size_t(L.rows) * size_t(L.NR) * 8);
+    L.off_slot = o;
+    o = align256(o + recs * 8);
+    L.off_skey = o;
+    o = align256(o + recs * 4);
+    L.off_crow = o;
+    o = align256(o + (recs + 1) * size_t(D) * 2);
+    L.off_slab = o;
+    o = align256(o + size_t(B) * size_t(L.NQB) * size_t(L.NR * L.RK) * size_t(D) * 4);
+    L.total = o;
+    return L;
+  }
   // the range kernel moves records in blocks of kRecBlock, which may run past
   // the last row's records: each record array is followed by one block of slack
-  size_t o = 0;
   L.off_rkd = o;
   o = align256(o + recs * 8 + kRecBlock * 8);
   L.off_rmask = o;
@@ -105,6 +139,9 @@ struct Problem {
   int* slot;  // int2 pairs
   uint16_t* qt;
   float* slab;
+  int* skey;    // slot-row route: key of each record
+  uint16_t* crow;  // slot-row route: bf16 dK row of each record; row rows*rec_stride takes padding
+
   int64_t rec_stride, RK, NR, NQB, QBS, nchunk, HP;
 };
 
@@ -132,5 +169,8 @@ hipError_t launch_rows_export(const Problem& P, hipStream_t stream);
 // Two-pass dK: range-major reduction into per query-block slabs, then the
 // fixed-order sum of the slabs into d_k.
 hipError_t launch_dk(const Problem& P, hipStream_t stream);
+// Slot-row dK: the records' dK rows summed per (32 keys, query block) in a
+// fixed order into the slabs, then the same slab sum.
+hipError_t launch_dk_rows(const Problem& P, hipStream_t stream);
 
 }  // namespace ibwd

@@ -96,6 +96,11 @@ extern "C" {
                                       the remainder), so that the output rounding is its only
                                       error of note.  Default route only; not with
                                       IBWD_FLAG_ATOMIC_DK, whose dK accumulates in d_k */
+#define IBWD_FLAG_DK_KEY_RANGES 16u /* deterministic dK by the key-range GEMM at any selection
+                                       density (by default a sparse call with topk*16 > S_k) */
+#define IBWD_FLAG_DK_SLOT_ROWS 32u  /* indexer_bwd_sparse only: deterministic dK from per-slot
+                                       rows at any density (by default when topk*16 <= S_k);
+                                       excludes IBWD_FLAG_DK_KEY_RANGES */
 
 /*
  * indexer_bwd_sparse — backward of the top-k (sparse) indexer.

@@ -59,6 +59,38 @@ def test_strerror_and_workspace():
     assert ibwd.indexer_bwd_workspace_bytes(False, 1, 64, 128, 4, 32, 129, 0) == 0   # topk > S_k
 
 
+def test_dk_route_flags_and_workspace():
+    """The deterministic dK route follows the selection density (slot rows when
+    topk*16 <= S_k) unless a flag forces one; the workspace follows the route."""
+    KR, SR = ibwd.IBWD_FLAG_DK_KEY_RANGES, ibwd.IBWD_FLAG_DK_SLOT_ROWS
+    wsb = ibwd.indexer_bwd_workspace_bytes
+    rows, NR, NQB = 8192, 32, 16
+    for topk, auto_rows in ((128, True), (256, True), (257, False), (1024, False)):
+        auto = wsb(False, 1, 8192, 4096, 64, 128, topk, 0)
+        kr = wsb(False, 1, 8192, 4096, 64, 128, topk, KR)
+        sr = wsb(False, 1, 8192, 4096, 64, 128, topk, SR)
+        assert auto == (sr if auto_rows else kr)
+        assert kr != sr
+        # slot rows: {position, dI} and a key per slot, a bf16 dK row per slot plus
+        # one, the range table, the per query-block slabs
+        slot_rows_bytes = (rows * topk * (8 + 4) + (rows * topk + 1) * 128 * 2 + rows * NR * 8
+                           + NQB * NR * 128 * 128 * 4)
+        assert slot_rows_bytes <= sr <= slot_rows_bytes + 5 * 256
+    # the dense call always takes the key ranges: the slot-row flag is an error there
+    assert wsb(True, 1, 64, 64, 4, 32, 0, SR) == 0
+    assert wsb(True, 1, 64, 64, 4, 32, 0, KR) == wsb(True, 1, 64, 64, 4, 32, 0, 0)
+    lib = ibwd.library()
+    base = [A, A + 0x100000, A + 0x200000, A + 0x400000, A + 0x500000, A + 0x600000, A + 0x700000,
+            A + 0x800000]
+    assert lib.indexer_bwd_dense(*base, 1, 16, 16, 4, 32, 0, 1.0, 1.0, SR, A + 0x1000000, 1 << 30,
+                                 None) == ibwd.IBWD_ERR_INVALID_ARGUMENT
+    # the binding names the routes
+    with pytest.raises(ValueError):
+        ibwd._flags(False, False, False, "sideways")
+    assert ibwd._flags(False, False, False, "slot_rows") == SR
+    assert ibwd._flags(True, False, True, "key_ranges") == KR | ibwd.IBWD_FLAG_DETERMINISTIC | ibwd.IBWD_FLAG_BF16_OUT
+
+
 # fake, 256-byte aligned "device" addresses: every case below must be rejected
 # by host-side validation, so nothing is dereferenced
 A = 0x10000000
@@ -83,7 +115,8 @@ def call_sparse(a):
     dict(q=None), dict(k=None), dict(w=None), dict(ids=None), dict(I=None), dict(p=None),
     dict(dq=None), dict(dw=None), dict(dk=None),
     dict(B=0), dict(S_q=0), dict(S_k=-1), dict(H=0), dict(H=65), dict(D=48), dict(D=256),
-    dict(topk=0), dict(topk=129), dict(topk=129, flags=2, ws=None, ws_bytes=0), dict(flags=3), dict(flags=7), dict(flags=10), dict(flags=16), dict(q=A + 8), dict(dk=A + 0x800004),
+    dict(topk=0), dict(topk=129), dict(topk=129, flags=2, ws=None, ws_bytes=0), dict(flags=3), dict(flags=7), dict(flags=10), dict(flags=64), dict(flags=48),
+    dict(flags=2 | 16, ws=None, ws_bytes=0), dict(flags=2 | 32, ws=None, ws_bytes=0), dict(q=A + 8), dict(dk=A + 0x800004),
     dict(w=A + 0x200002), dict(ws=None, ws_bytes=0), dict(ws=A + 0x900000, ws_bytes=16),
     dict(ws=A + 0x900010, ws_bytes=1 << 30), dict(flags=1, ws=None, ws_bytes=1 << 30),
     dict(B=1 << 20, S_q=1 << 20, H=64, D=128), dict(S_k=1024 * 256 + 1, D=128, ws_bytes=1 << 40),
@@ -123,7 +156,8 @@ def test_valid_arguments_without_gpu_fail_cleanly():
               sparse_args(flags=G), sparse_args(flags=G | ibwd.IBWD_FLAG_DETERMINISTIC),
               sparse_args(flags=G | ibwd.IBWD_FLAG_ATOMIC_DK, ws=None, ws_bytes=0),
               sparse_args(flags=ibwd.IBWD_FLAG_BF16_OUT),
-              sparse_args(flags=G | ibwd.IBWD_FLAG_BF16_OUT | ibwd.IBWD_FLAG_DETERMINISTIC)):
+              sparse_args(flags=G | ibwd.IBWD_FLAG_BF16_OUT | ibwd.IBWD_FLAG_DETERMINISTIC),
+              sparse_args(flags=ibwd.IBWD_FLAG_DK_SLOT_ROWS), sparse_args(flags=ibwd.IBWD_FLAG_DK_KEY_RANGES)):
         assert call_sparse(a) in (ibwd.IBWD_ERR_HIP, ibwd.IBWD_ERR_UNSUPPORTED_DEVICE)
 
 

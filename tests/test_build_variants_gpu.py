@@ -2,7 +2,8 @@
 
 The library's kernels keep short buffer rings: the row kernel two K tiles,
 four slot stages and two sign-word buffers; the range kernel three Q' tiles,
-two key tables and four record stages.  The deep-buffer build
+two key tables and four record stages (the slot-row route stages its dK rows
+in a K tile of the ring).  The deep-buffer build
 (IBWD_DEEP_BUFFERS, libdsa_indexer_bwd_deepbuf.so) keeps 4/8/4 and 4/4/8 of
 them with the same copy schedule, so none of its buffers is reused within a
 copy's window.  A buffer the library reused too early (a missing wait or
@@ -10,7 +11,8 @@ barrier) would change its results and not the variant's: every output of the
 two builds must be equal bit for bit, d_k included (the summation order does
 not depend on the ring depth).  Cases: full-size workloads (long query loops
 per key range), duplicate ids (the range kernel's ordered fallback pass),
-short and ragged rows, bf16 outputs, one head group (H <= 32) at D = 64.
+short and ragged rows, bf16 outputs, one head group (H <= 32) at D = 64, on
+both deterministic dK routes where they differ.
 """
 import dataclasses
 
@@ -55,36 +57,38 @@ def assert_same_bits(name, a, b):
     log(f"{name}: library and deep-buffer build bitwise equal")
 
 
-@pytest.mark.parametrize("name", ["anchor", "dense", "wide"])
+@pytest.mark.parametrize("name", ["anchor", "dense", "wide", "anchor-topk256"])
 def test_full_size_workloads(ibwd, name):
     log(f"case: build variants, full-size {name}")
-    x = make_inputs(name)
+    x = make_inputs(dataclasses.replace(WORKLOADS["anchor"], topk=256) if name == "anchor-topk256" else name)
     assert_same_bits(name, *both_builds(ibwd, x))
 
 
-def test_duplicate_ids(ibwd):
+@pytest.mark.parametrize("route", ["key_ranges", "slot_rows"])
+def test_duplicate_ids(ibwd, route):
     """Rows that select keys two or three times: the range kernel adds the
     losing records in its ordered fallback pass."""
-    log("case: build variants, duplicate ids")
+    log(f"case: build variants, duplicate ids route={route}")
     x = make_inputs("anchor", S_q=1024, seed=91)
     ids = x.ids.copy()
     ids[:, :, 1::9] = ids[:, :, 0::9][:, :, :ids[:, :, 1::9].shape[2]]
     ids[:, ::5, 2::9] = ids[:, ::5, 0::9][:, :, :ids[:, ::5, 2::9].shape[2]]
     x.ids = ids
-    assert_same_bits("duplicates", *both_builds(ibwd, x))
+    assert_same_bits(f"duplicates-{route}", *both_builds(ibwd, x, dk_route=route))
 
 
-def test_short_ragged_rows(ibwd):
+@pytest.mark.parametrize("route", ["key_ranges", "slot_rows"])
+def test_short_ragged_rows(ibwd, route):
     """topk 128 at the anchor's shapes with row t keeping min(t/2 + 1, 128)
     slots (a -1 tail): many empty (query, range) pairs and short chunk loops."""
-    log("case: build variants, short ragged rows")
+    log(f"case: build variants, short ragged rows route={route}")
     wl = dataclasses.replace(WORKLOADS["anchor"], S_q=2048, topk=128)
     x = make_inputs(wl, seed=92)
     ids = x.ids.copy()
     for t in range(ids.shape[1]):
         ids[:, t, min(t // 2 + 1, ids.shape[2]):] = -1
     x.ids = ids
-    assert_same_bits("ragged", *both_builds(ibwd, x))
+    assert_same_bits(f"ragged-{route}", *both_builds(ibwd, x, dk_route=route))
 
 
 def test_bf16_outputs(ibwd):
@@ -93,9 +97,10 @@ def test_bf16_outputs(ibwd):
     assert_same_bits("bf16", *both_builds(ibwd, x, bf16_out=True))
 
 
-def test_one_head_group(ibwd):
+@pytest.mark.parametrize("route", ["key_ranges", "slot_rows"])
+def test_one_head_group(ibwd, route):
     """H = 32 (one wave per row in the row kernel) at D = 64."""
-    log("case: build variants, H=32 D=64")
+    log(f"case: build variants, H=32 D=64 route={route}")
     wl = dataclasses.replace(WORKLOADS["sparse"], H=32, D=64, S_q=2048)
     x = make_inputs(wl, seed=94)
-    assert_same_bits("h32d64", *both_builds(ibwd, x))
+    assert_same_bits(f"h32d64-{route}", *both_builds(ibwd, x, dk_route=route))

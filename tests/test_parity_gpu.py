@@ -67,9 +67,10 @@ def host(r):
             else a.cpu().numpy() for a in r]
 
 
-def run(ibwd, x, t=None, deterministic=False, atomic_dk=False, bf16_out=False):
+def run(ibwd, x, t=None, deterministic=False, atomic_dk=False, bf16_out=False, dk_route="auto"):
     t = dev_inputs(x) if t is None else t
-    r = call(ibwd, x, t, deterministic=deterministic, atomic_dk=atomic_dk, bf16_out=bf16_out)
+    kw = {} if dk_route == "auto" else dict(dk_route=dk_route)
+    r = call(ibwd, x, t, deterministic=deterministic, atomic_dk=atomic_dk, bf16_out=bf16_out, **kw)
     torch.cuda.synchronize()
     return host(r)
 
@@ -113,32 +114,38 @@ def test_workload_shapes_reduced_queries(ibwd, name, S_q):
     assert_parity(f"{name}-Sq{S_q}", run(ibwd, x), oracle.Problem.from_inputs(x).backward())
 
 
+ROUTES = ["key_ranges", "slot_rows"]
+
+
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("topk,H,D,pad", [(1, 4, 32, 0.0), (37, 64, 128, 0.1), (100, 33, 64, 0.3),
                                           (129, 1, 32, 0.05), (300, 64, 64, 0.5), (16, 17, 128, 1.0)])
-def test_ragged_and_odd_shapes(ibwd, topk, H, D, pad):
+def test_ragged_and_odd_shapes(ibwd, topk, H, D, pad, route):
     """topk not a multiple of any chunk, H below/above MFMA tiles, every D, heavy
-    padding, an all-padding workload."""
-    log(f"case: ragged topk={topk} H={H} D={D} pad={pad}")
+    padding, an all-padding workload; both deterministic dK routes."""
+    log(f"case: ragged topk={topk} H={H} D={D} pad={pad} route={route}")
     wl = dataclasses.replace(WORKLOADS["tiny"], H=H, D=D, S_q=48, S_k=max(160, topk + 1), topk=topk,
                              pad_frac=pad)
     x = make_inputs(wl, seed=7 + topk)
-    got = run(ibwd, x)
+    got = run(ibwd, x, dk_route=route)
     ref = oracle.Problem.from_inputs(x).backward()
     if pad >= 1.0:
         assert all(np.all(a == 0) for a in got)
         return
-    assert_parity(f"ragged-{topk}-{H}-{D}", got, ref)
+    assert_parity(f"ragged-{topk}-{H}-{D}-{route}", got, ref)
 
 
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("S_k,topk", [(40000, 700), (262144, 300)])
-def test_many_key_ranges(ibwd, S_k, topk):
+def test_many_key_ranges(ibwd, S_k, topk, route):
     """More than 64 key ranges of 128 keys (313, and 2048 at the largest S_k the
     library accepts): the range scan with several ranges per lane, range ids of
-    up to 11 bits in the ballot ranking, and many range workgroups."""
-    log(f"case: many ranges S_k={S_k} topk={topk}")
+    up to 11 bits in the ballot ranking, and many range (or key-block) workgroups."""
+    log(f"case: many ranges S_k={S_k} topk={topk} route={route}")
     wl = dataclasses.replace(WORKLOADS["tiny"], H=8, D=32, S_q=24, S_k=S_k, topk=topk, pad_frac=0.05)
     x = make_inputs(wl, seed=S_k % 1000 + topk)
-    assert_parity(f"ranges-{S_k}-{topk}", run(ibwd, x), oracle.Problem.from_inputs(x).backward())
+    assert_parity(f"ranges-{S_k}-{topk}-{route}", run(ibwd, x, dk_route=route),
+                  oracle.Problem.from_inputs(x).backward())
 
 
 def test_batches_local_ids_do_not_alias(ibwd):
@@ -171,13 +178,13 @@ def test_dense_q_offset(ibwd, q_offset):
         return
     assert_parity(f"dense-off{q_offset}", got, ref)
 
-@pytest.mark.parametrize("atomic_dk", [False, True])
-def test_global_ids(ibwd, atomic_dk):
+@pytest.mark.parametrize("atomic_dk,route", [(False, "key_ranges"), (False, "slot_rows"), (True, "auto")])
+def test_global_ids(ibwd, atomic_dk, route):
     """B=3 with global ids (key id - b*S_k of batch b): the valid slots of the
     local-id case shifted by b*S_k, and its padding slots replaced by keys of
     the other batches, ids past B*S_k and negatives.  Equal to the local-id
     call (bitwise on the default route) and to the oracle on the remapped ids."""
-    log(f"case: B=3 global ids atomic={atomic_dk}")
+    log(f"case: B=3 global ids atomic={atomic_dk} route={route}")
     wl = dataclasses.replace(WORKLOADS["tiny"], B=3, S_q=40, S_k=300, topk=96, pad_frac=0.3)
     x = make_inputs(wl, seed=41)
     S_k = wl.S_k
@@ -190,11 +197,11 @@ def test_global_ids(ibwd, atomic_dk):
     local = oracle.global_ids_to_local(g, S_k)
     assert np.array_equal(local, np.where(pad, -1, x.ids))
     t = dev_inputs(x)
-    ref_local = run(ibwd, x, t, atomic_dk=atomic_dk)
+    ref_local = run(ibwd, x, t, atomic_dk=atomic_dk, dk_route=route)
     tg = dict(t, ids=torch.from_numpy(g).to(t["q"].device))
     got = ibwd.indexer_bwd_sparse(tg["q"], tg["k"], tg["w"], tg["ids"], tg["I"], tg["p"],
                                   sm_scale=x.sm_scale, grad_loss=x.grad_loss, atomic_dk=atomic_dk,
-                                  global_ids=True)
+                                  global_ids=True, dk_route=route)
     torch.cuda.synchronize()
     got = [a.cpu().numpy() for a in got]
     assert np.array_equal(got[0], ref_local[0]) and np.array_equal(got[1], ref_local[1])
@@ -203,16 +210,19 @@ def test_global_ids(ibwd, atomic_dk):
     else:
         assert np.array_equal(got[2], ref_local[2])
     x.ids = local
-    assert_parity(f"global-atomic{int(atomic_dk)}", got, oracle.Problem.from_inputs(x).backward())
+    assert_parity(f"global-atomic{int(atomic_dk)}-{route}", got, oracle.Problem.from_inputs(x).backward())
 
 
-@pytest.mark.parametrize("name,S_q", [("tiny", 64), ("anchor", 192), ("dense", 160)])
-def test_bf16_outputs(ibwd, name, S_q):
+@pytest.mark.parametrize("name,S_q,topk", [("tiny", 64, 0), ("anchor", 192, 0), ("dense", 160, 0),
+                                           ("anchor", 192, 128)])
+def test_bf16_outputs(ibwd, name, S_q, topk):
     """bf16 outputs within the same bars as fp32 outputs (not widened): d_w and
     d_k are the fp32 outputs of the same call rounded to nearest even, bit for
-    bit; d_q is rounded from a dQ whose G' enters GEMM2 as two bf16 terms."""
-    log(f"case: bf16 outputs {name} S_q={S_q}")
-    x = make_inputs(name, S_q=S_q, seed=51)
+    bit; d_q is rounded from a dQ whose G' enters GEMM2 as two bf16 terms.
+    topk 128 of 4096 keys takes the slot-row dK route."""
+    log(f"case: bf16 outputs {name} S_q={S_q} topk={topk}")
+    wl = dataclasses.replace(WORKLOADS[name], S_q=S_q, **({"topk": topk} if topk else {}))
+    x = make_inputs(wl, seed=51)
     t = dev_inputs(x)
     f32 = run(ibwd, x, t)
     b16 = run(ibwd, x, t, bf16_out=True)
@@ -221,7 +231,7 @@ def test_bf16_outputs(ibwd, name, S_q):
     assert np.array_equal(b16[1], bf16_rne_bits(f32[1]))
     assert np.array_equal(b16[2], bf16_rne_bits(f32[2]))
     ref = oracle.Problem.from_inputs(x).backward()
-    e = assert_parity(f"bf16-{name}", [bf16_bits_to_f32(b) for b in b16], ref)
+    e = assert_parity(f"bf16-{name}-{topk}", [bf16_bits_to_f32(b) for b in b16], ref)
     # every d_q element is the oracle's value up to one rounding to bf16 (half a
     # unit in the last place, 2^-8 relative) and fp32 accumulation error: the
     # G' of its product lost nothing to bf16
@@ -232,15 +242,16 @@ def test_bf16_outputs(ibwd, name, S_q):
         np.abs(dq - rq) - BF16_U * np.abs(rq))
 
 
-@pytest.mark.parametrize("bf16_out", [False, True])
-def test_graph_capture_replays(ibwd, bf16_out):
+@pytest.mark.parametrize("bf16_out,topk", [(False, 1024), (True, 1024), (False, 128)])
+def test_graph_capture_replays(ibwd, bf16_out, topk):
     """The call captured in a HIP graph (the library enqueues kernels only, no
     allocation, memset or host synchronisation): every replay, with eager
     library calls on other inputs and synchronisations in between, is bitwise
     equal to the eager call."""
-    log(f"case: graph capture bf16_out={bf16_out}")
-    x = make_inputs("anchor", S_q=256, seed=61)
-    y = make_inputs("anchor", S_q=256, seed=62)
+    log(f"case: graph capture bf16_out={bf16_out} topk={topk}")
+    wl = dataclasses.replace(WORKLOADS["anchor"], topk=topk)
+    x = make_inputs(wl, S_q=256, seed=61)
+    y = make_inputs(wl, S_q=256, seed=62)
     tx, ty = dev_inputs(x), dev_inputs(y)
     ref = run(ibwd, x, tx, bf16_out=bf16_out)
     dt = torch.bfloat16 if bf16_out else torch.float32
@@ -289,15 +300,21 @@ def test_padding_equivalence(ibwd):
     assert relrms(alt[2], base[2]) < 1e-6
 
 
-def test_run_to_run_bitwise(ibwd):
-    """The default route is bitwise reproducible for all three outputs."""
-    log("case: run-to-run determinism (default route)")
-    x = make_inputs("anchor", S_q=256, seed=13)
+@pytest.mark.parametrize("topk", [1024, 128])
+def test_run_to_run_bitwise(ibwd, topk):
+    """Both deterministic routes (the key-range route at topk 1024, the slot-row
+    route at 128 of 4096 keys) are bitwise reproducible for all three outputs;
+    d_q and d_w do not depend on the route."""
+    log(f"case: run-to-run determinism topk={topk}")
+    wl = dataclasses.replace(WORKLOADS["anchor"], topk=topk)
+    x = make_inputs(wl, S_q=256, seed=13)
     t = dev_inputs(x)
     a = run(ibwd, x, t)
     b = run(ibwd, x, t, deterministic=True)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+    other = run(ibwd, x, t, dk_route="key_ranges" if topk == 128 else "slot_rows")
+    assert np.array_equal(other[0], a[0]) and np.array_equal(other[1], a[1])
 
 
 @pytest.mark.parametrize("name", ["tiny", "anchor", "dense"])
@@ -315,14 +332,14 @@ def test_atomic_route(ibwd, name):
     assert np.array_equal(a[0], d[0]) and np.array_equal(a[1], d[1])
 
 
-@pytest.mark.parametrize("atomic_dk", [False, True])
+@pytest.mark.parametrize("atomic_dk,route", [(False, "key_ranges"), (False, "slot_rows"), (True, "auto")])
 @pytest.mark.parametrize("S_k,topk", [(300, 200), (4096, 96)])
-def test_duplicate_ids(ibwd, atomic_dk, S_k, topk):
+def test_duplicate_ids(ibwd, atomic_dk, route, S_k, topk):
     """Duplicate ids in a row are independent slots (both routes; the default
     route's range kernel takes its ordered path for tiles with repeated keys).
     At 96 of 4096 keys the range kernel's waves also pass over key blocks
     without a record of the query."""
-    log(f"case: duplicate ids atomic={atomic_dk} S_k={S_k} topk={topk}")
+    log(f"case: duplicate ids atomic={atomic_dk} route={route} S_k={S_k} topk={topk}")
     wl = dataclasses.replace(WORKLOADS["anchor"], S_q=48, S_k=S_k, topk=topk, pad_frac=0.05)
     x = make_inputs(wl, seed=31 + topk)
     rng = np.random.default_rng(5)
@@ -332,21 +349,22 @@ def test_duplicate_ids(ibwd, atomic_dk, S_k, topk):
         dst = rng.integers(0, wl.topk, size=wl.topk // 3)
         x.ids[0, t, dst] = x.ids[0, t, src]
     x.ids[0, 0, :] = 7          # a row of one key repeated
-    got = run(ibwd, x, atomic_dk=atomic_dk)
-    assert_parity(f"dup-atomic{int(atomic_dk)}-{S_k}", got, oracle.Problem.from_inputs(x).backward())
+    got = run(ibwd, x, atomic_dk=atomic_dk, dk_route=route)
+    assert_parity(f"dup-atomic{int(atomic_dk)}-{route}-{S_k}", got, oracle.Problem.from_inputs(x).backward())
 
 
-def test_ragged_row_lengths(ibwd):
+@pytest.mark.parametrize("route", ROUTES)
+def test_ragged_row_lengths(ibwd, route):
     """Per-row valid lengths that ramp up with the query (row t keeps its first
     min(t//2 + 1, topk) slots, the rest are -1), at the anchor's H, D, S_k and
     topk: every chunk count from 1 to the full row, a partial last chunk."""
-    log("case: ragged row-length ramp")
+    log(f"case: ragged row-length ramp route={route}")
     wl = dataclasses.replace(WORKLOADS["anchor"], S_q=2048, pad_frac=0.0)
     x = make_inputs(wl, seed=51)
     t = np.arange(wl.S_q)[:, None]
     j = np.arange(wl.topk)[None, :]
     x.ids[0][j >= np.minimum(t // 2 + 1, wl.topk)] = -1
-    assert_parity("ramp", run(ibwd, x), oracle.Problem.from_inputs(x).backward())
+    assert_parity(f"ramp-{route}", run(ibwd, x, dk_route=route), oracle.Problem.from_inputs(x).backward())
 
 
 @pytest.mark.parametrize("pad", [0.0, 0.4])
@@ -397,10 +415,12 @@ def test_invalid_call_leaves_outputs_untouched(ibwd):
 # of d_q, d_w and d_k against the full oracle backward (seconds on the host
 # cores)
 
-@pytest.mark.parametrize("name", ["sparse", "anchor", "wide", "dense"])
+@pytest.mark.parametrize("name", ["sparse", "anchor", "wide", "dense", "anchor-topk128"])
 def test_full_size_workload(ibwd, name):
+    """The four workloads, and the anchor at topk 128 (the slot-row dK route)."""
     log(f"case: full-size {name}")
-    x = make_inputs(name, device="cuda:0")
+    wl = dataclasses.replace(WORKLOADS["anchor"], topk=128) if name == "anchor-topk128" else name
+    x = make_inputs(wl, device="cuda:0")
     got = run(ibwd, x)
     ref = oracle.Problem.from_inputs(x).backward()
     assert_parity(f"full-{name}", got, ref)
@@ -413,14 +433,16 @@ def test_full_size_workload(ibwd, name):
     assert e < 6e-3, e
 
 
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("topk", [128, 256, 384, 640, 1536])
-def test_topk_sweep_anchor_shapes(ibwd, topk):
+def test_topk_sweep_anchor_shapes(ibwd, topk, route):
     """The topk sweep points at the anchor's H, D and S_k (256 queries, 2%
-    padding): every element against the oracle."""
-    log(f"case: topk sweep {topk}")
+    padding), on both deterministic dK routes: every element against the oracle."""
+    log(f"case: topk sweep {topk} route={route}")
     wl = dataclasses.replace(WORKLOADS["anchor"], S_q=256, topk=topk)
     x = make_inputs(wl, seed=300 + topk)
-    assert_parity(f"topk-{topk}", run(ibwd, x), oracle.Problem.from_inputs(x).backward())
+    assert_parity(f"topk-{topk}-{route}", run(ibwd, x, dk_route=route),
+                  oracle.Problem.from_inputs(x).backward())
 
 
 def test_side_stream_without_workspace(ibwd):
@@ -446,16 +468,20 @@ def test_stage_hook_reports_every_kernel(ibwd):
     """The profiling hook runs once per enqueued kernel, in launch order, on both routes."""
     log("case: stage hook")
     x = make_inputs("tiny", seed=3)
+    y = make_inputs(dataclasses.replace(WORKLOADS["anchor"], S_q=64, topk=128), seed=3)
     seen = []
     ibwd.set_stage_hook(lambda stage, name: seen.append((stage, name)))
     try:
         a = run(ibwd, x)
         b = run(ibwd, x, atomic_dk=True)
+        run(ibwd, y)  # 128 of 4096 keys: the slot-row route by density
     finally:
         ibwd.set_stage_hook(None)
     assert seen == [(0, "row_prep_kernel"), (1, "row_export_kernel"), (2, "dk_range_kernel"),
-                    (3, "dk_sum_kernel"), (0, "zero_u32_kernel"), (1, "row_kernel")]
+                    (3, "dk_sum_kernel"), (0, "zero_u32_kernel"), (1, "row_kernel"),
+                    (0, "row_prep_kernel"), (1, "row_export_kernel"), (2, "dk_rows_kernel"),
+                    (3, "dk_sum_kernel")]
     c = run(ibwd, x)  # hook removed: nothing more is reported
-    assert len(seen) == 6
+    assert len(seen) == 10
     assert all(np.array_equal(u, v) for u, v in zip(a, c))
     assert_parity("hook-atomic", b, oracle.Problem.from_inputs(x).backward())
