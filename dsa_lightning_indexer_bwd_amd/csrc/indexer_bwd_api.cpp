@@ -79,14 +79,16 @@ int route_force(uint32_t flags) {
   return (flags & IBWD_FLAG_DK_SLOT_ROWS) ? 2 : (flags & IBWD_FLAG_DK_KEY_RANGES) ? 1 : 0;
 }
 
-bool slot_rows(int64_t S_k, int64_t row_len, bool dense, uint32_t flags) {
-  return ibwd::use_slot_rows(S_k, row_len, dense, route_force(flags));
+bool slot_rows(int64_t B, int64_t S_q, int64_t S_k, int64_t D, int64_t row_len, bool dense,
+               uint32_t flags) {
+  return ibwd::use_slot_rows(B, S_q, S_k, D, row_len, dense, route_force(flags));
 }
 
 size_t workspace_bytes(int64_t B, int64_t S_q, int64_t S_k, int64_t H, int64_t D,
                        int64_t row_len, bool dense, uint32_t flags) {
   if (flags & IBWD_FLAG_ATOMIC_DK) return 0;
-  return ibwd::make_layout(B, S_q, S_k, H, D, row_len, slot_rows(S_k, row_len, dense, flags)).total;
+  return ibwd::make_layout(B, S_q, S_k, H, D, row_len, slot_rows(B, S_q, S_k, D, row_len, dense, flags))
+      .total;
 }
 
 // Both sparse entry points: every check first, then the launch.  noalloc: the
@@ -101,6 +103,9 @@ int sparse_call(const void* q, const void* k, const float* w, const int32_t* top
   if (st != IBWD_OK) return st;
   if (!topk_ids || !aligned(topk_ids, 4)) return IBWD_ERR_INVALID_ARGUMENT;
   if (topk > S_k) return IBWD_ERR_INVALID_ARGUMENT;  // more slots than keys
+  // the slot-row route keeps all dK rows within 4 GiB
+  if ((flags & IBWD_FLAG_DK_SLOT_ROWS) && !ibwd::slot_rows_fit(B, S_q, D, topk))
+    return IBWD_ERR_INVALID_ARGUMENT;
   const size_t need = workspace_bytes(B, S_q, S_k, H, D, topk, false, flags);
   if (noalloc) {
     if (need > ibwd::kNoAllocScratchBytes) return IBWD_ERR_INVALID_ARGUMENT;
@@ -134,7 +139,7 @@ int sparse_call(const void* q, const void* k, const float* w, const int32_t* top
   P.sm_scale = sm_scale;
   P.grad_loss = grad_loss;
   P.route = (flags & IBWD_FLAG_ATOMIC_DK)         ? ibwd::kDkAtomic
-            : slot_rows(S_k, topk, false, flags) ? ibwd::kDkSlotRows
+            : slot_rows(B, S_q, S_k, D, topk, false, flags) ? ibwd::kDkSlotRows
                                                  : ibwd::kDkTwoPass;
   return ibwd::launch(P, workspace, stream) == hipSuccess ? IBWD_OK : IBWD_ERR_HIP;
 }
@@ -213,6 +218,7 @@ size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_
   if (D != 32 && D != 64 && D != 128) return 0;
   if (!fits(B, S_q, H, D) || !fits(B, S_k, D) || !fits(B, S_q, row_len)) return 0;
   if (dense && (flags & IBWD_FLAG_DK_SLOT_ROWS)) return 0;
+  if (!dense && (flags & IBWD_FLAG_DK_SLOT_ROWS) && !ibwd::slot_rows_fit(B, S_q, D, row_len)) return 0;
   return workspace_bytes(B, S_q, S_k, H, D, row_len, dense != 0, flags);
 }
 

@@ -583,141 +583,253 @@ __global__ __launch_bounds__(256) void dk_sum_kernel(Problem P) {
   }
 }
 
-// Slot-row route: one wave per (32-key block of a key range, query block,
-// batch).  The row kernel left, for every valid slot, its key and its dK row
-// C = dI * sum_h [S > 0] (w*q) in bf16 at its record position (the prep kernel
-// groups a row's records by key range, slot order within a range).  The wave
-// walks the query block's queries in order, 64 at a time: their {first, end}
-// of this range give a run of records per query, numbered across the 64
-// queries by a prefix sum; each lane takes one record of the run (its query by
-// a binary search over the run starts), reads its key, and a ballot picks the
-// records of the wave's 32 keys.  Keys are read 256 records at a time, the
-// picked records queued in LDS, and their rows read 16 at a time with the next
-// 16 in flight, and added in fp32, in (query, position) order, into the wave's
-// 32 x D partial dK, which it holds in registers (lane l: columns
-// E*l .. E*l+E-1 of every key; the key, uniform over the wave, indexes the
-// registers).  The order is fixed, so the result does not depend on
-// scheduling.  The partial dK then goes to the query block's slab.
-constexpr int kRowBlocks = 16;               // key blocks per range in the slot-row sum
-constexpr int KW = kRangeKeys / kRowBlocks;  // keys per wave
+// Slot-row route: one workgroup of four waves per (key range, query block,
+// batch); wave s owns keys 32s .. 32s+31 of the range.  The row kernel left,
+// for every valid slot, its key and its dK row C = dI * sum_h [S > 0] (w*q) in
+// bf16 at its record position (the prep kernel groups a row's records by key
+// range, slot order within a range).  The range's records of the query block
+// form one sequence: query by query, each query's run [first, end) of its row;
+// the workgroup numbers it once (a prefix sum of the run lengths, in LDS).
+// Rounds of 1024 records: wave w reads the keys of records 256w .. 256w+255 of
+// the round (the query of a record by a binary search over the run starts),
+// and queues them in LDS by key block, in record order.  After a barrier wave
+// s takes its block's records from the queues of waves 0..3 in turn, that is
+// in record order, 16 at a time: their rows are copied from global memory
+// straight into LDS (global_load_lds, three batches in flight), and the batch
+// is added with one v_mfma 32x32x16 per 32 columns,
+//   acc[key][d] += sum_k onehot[key][k] * row_k[d],
+// the one-hot A operand (1.0 where record k is of the key) read from a small
+// LDS table, the rows read transposed as the B operand.  The products are
+// exact and the sums run in the matrix cores' fixed order, so d_k does not
+// depend on scheduling.  Each wave reads the keys of the next round before it
+// adds the rows of the current one.  The partial dK then goes to the query
+// block's slab.
+constexpr int kRowWaves = kRangeKeys / 32;  // key blocks of 32 per range
 template <int D>
-__global__ __launch_bounds__(64) void dk_rows_kernel(Problem P) {
-  constexpr int E = D >= 128 ? 2 : 1;  // bf16 of a row per lane
-  constexpr int NL = D / E;            // lanes covering a row (32 at D = 32)
-  constexpr int kBatch = 16;           // row reads per batch (two batches in flight)
-  constexpr int kPiece = 4;            // 64-record chunks whose keys are read together
-  __shared__ int ex_s[64], base_s[64];
-  __shared__ int2 queue[kPiece * 64];  // selected {record, key - k0} of a piece
-  const int lane = threadIdx.x;
-  const int lc = lane < NL ? lane : 0;
-  const int blk = int(blockIdx.x) % kRowBlocks;
-  const int rg = int(blockIdx.x) / kRowBlocks;
+__global__ __launch_bounds__(64 * kRowWaves) void dk_rows_kernel(Problem P) {
+  constexpr int kScan = 4;             // 64-record chunks a wave scans per round
+  constexpr int kRound = 64 * kScan * kRowWaves;
+  __shared__ int ex_s[kMaxQueryBlock + 1];  // start of each query's run in the sequence
+  __shared__ int base_s[kMaxQueryBlock];    // record index of each run's first record
+  __shared__ int2 queue[2][kRowWaves][64 * kScan];  // {record, key - 32s}, by block, in order
+  __shared__ int qoff[2][kRowWaves][kRowWaves];      // [buf][scanning wave][block] start
+  __shared__ int qcnt[2][kRowWaves][kRowWaves];
+  __shared__ int wsum[kRowWaves];
+  // staged rows of a batch, [16][D] bf16, 16-byte chunks XORed by the row so
+  // that the four rows of a transposed read fall on distinct banks
+  constexpr int RP = 2 * D;       // row pitch, bytes
+  constexpr int CPR = RP / 16;    // 16-byte chunks per row
+  constexpr int RPB = 256 / RP;   // rows per 256 bytes
+  constexpr int kDmaB = CPR / 4;  // 1 KiB copies per batch
+  constexpr int kStages = 3;      // batches in flight
+  constexpr int ND = D / 32;      // 32-column blocks
+  __shared__ __attribute__((aligned(16))) unsigned char stage_s[kRowWaves][kStages][16 * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t onehot_s[kRowWaves][32 * 16];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int rg = int(blockIdx.x);
   const int qb = int(blockIdx.y);
   const int64_t b = blockIdx.z;
-  const int k0 = rg * kRangeKeys + KW * blk;
-  // acc0[k], acc1[k]: this lane's columns E*lane, E*lane + 1 of key k0 + k
-  typedef float f32xkw_t __attribute__((ext_vector_type(KW)));
-  f32xkw_t acc0 = f32xkw_t{}, acc1 = f32xkw_t{};
+  const int R0 = rg * kRangeKeys;
   const int64_t t0 = int64_t(qb) * P.QBS;
-  const int64_t t1 = t0 + P.QBS < P.S_q ? t0 + P.QBS : P.S_q;
+  const int nq = int((t0 + P.QBS < P.S_q ? t0 + P.QBS : P.S_q) - t0);
   const int2* offs = reinterpret_cast<const int2*>(P.offs);
-  auto load_fe = [&](int64_t tb) -> int2 {
-    const int64_t t = tb + lane;
-    return t < t1 ? offs[(b * P.S_q + t) * P.NR + rg] : make_int2(0, 0);
-  };
-  // record f of the current run: its global record index (or 0) and key (or -1)
-  auto locate = [&](int f, int T, int& rec) -> int {
+
+  // ---- the sequence: run starts of the block's queries ---------------------
+  // thread i takes queries 2i, 2i+1 (nq <= 512)
+  int n2[2], f2[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = 2 * int(threadIdx.x) + u;
+    const int2 fe = q < nq ? offs[(b * P.S_q + t0 + q) * P.NR + rg] : make_int2(0, 0);
+    n2[u] = fe.y - fe.x;
+    f2[u] = fe.x;
+  }
+  int incl = n2[0] + n2[1];
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) {
+    const int v = wsum[w];
+    before += w < wv ? v : 0;
+    total += v;
+  }
+  {
+    const int ex = before + incl - n2[0] - n2[1];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = 2 * int(threadIdx.x) + u;
+      if (q < nq) {
+        ex_s[q] = ex + (u ? n2[0] : 0);
+        base_s[q] = int((b * P.S_q + t0 + q) * P.rec_stride) + f2[u];
+      }
+    }
+  }
+  __syncthreads();
+  const int T = __builtin_amdgcn_readfirstlane(total);
+
+  // record f of the sequence: its global record index (or 0) and key (or -1)
+  auto locate = [&](int f, int& rec) -> int {
     int lo = 0;
 #pragma unroll
-    for (int st = 32; st > 0; st >>= 1)
-      if (ex_s[lo + st] <= f) lo += st;  // a query without records shares its start with the next
+    for (int st = kMaxQueryBlock / 2; st > 0; st >>= 1)
+      if (lo + st < nq && ex_s[lo + st] <= f) lo += st;  // a query without records shares its start with the next
     rec = f < T ? base_s[lo] + (f - ex_s[lo]) : 0;
     return f < T ? P.skey[rec] : -1;
   };
-  auto row_at = [&](int rec) -> uint32_t {
-    const uint16_t* src = P.crow + int64_t(rec) * D + E * lc;
-    return E == 2 ? *reinterpret_cast<const uint32_t*>(src) : uint32_t(*src);
+  f32x16_t acc[ND];  // lane: column 32nb + l32, registers 4i + rr: key 8i + 4half + rr
+#pragma unroll
+  for (int nb = 0; nb < ND; ++nb) acc[nb] = f32x16_t{};
+  const int l32 = lane & 31, half = lane >> 5;
+  for (int i = lane; i < 32 * 16; i += 64) onehot_s[wv][i] = 0;
+  auto st_at = [](int r, int byte) {
+    return r * RP + (((byte >> 4) ^ (((r / RPB) & 3) * (CPR / 4))) << 4) + (byte & 15);
   };
-  // acc[kl] += row; kl is uniform over the wave, so the indexed register
-  // update needs no per-lane selection (-1: nothing)
-  auto add_row = [&](int kl, uint32_t v) {
-    if (kl >= 0) {
-      acc0[kl] += E == 2 ? bf16_lo(v) : __uint_as_float(v << 16);
-      if (E == 2) acc1[kl] += bf16_hi(v);
+  const uint32_t stage0 =
+      uint32_t(uintptr_t((__attribute__((address_space(3))) unsigned char*)(&stage_s[wv][0][0])));
+  int recs[kScan], keys[kScan];
+  auto scan_issue = [&](int round) {
+#pragma unroll
+    for (int c = 0; c < kScan; ++c) keys[c] = locate(round * kRound + (kScan * wv + c) * 64 + lane, recs[c]);
+  };
+  // this wave's records of the round, by key block, into queue[buf][wv]
+  auto scan_queue = [&](int buf) {
+    uint64_t m[kScan][kRowWaves];
+    int cnt[kRowWaves];
+#pragma unroll
+    for (int s2 = 0; s2 < kRowWaves; ++s2) cnt[s2] = 0;
+#pragma unroll
+    for (int c = 0; c < kScan; ++c) {
+      const int blk = keys[c] >= 0 ? (keys[c] - R0) >> 5 : -1;
+#pragma unroll
+      for (int s2 = 0; s2 < kRowWaves; ++s2) {
+        m[c][s2] = ballot(blk == s2);
+        cnt[s2] += __popcll(m[c][s2]);
+      }
+    }
+    int run[kRowWaves];
+    int o = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < kRowWaves; ++s2) {
+      run[s2] = o;
+      if (lane == 0) {
+        qoff[buf][wv][s2] = o;
+        qcnt[buf][wv][s2] = cnt[s2];
+      }
+      o += cnt[s2];
+    }
+#pragma unroll
+    for (int c = 0; c < kScan; ++c) {
+      const int blk = keys[c] >= 0 ? (keys[c] - R0) >> 5 : -1;
+#pragma unroll
+      for (int s2 = 0; s2 < kRowWaves; ++s2) {
+        if (blk == s2)
+          queue[buf][wv][run[s2] + __popcll(m[c][s2] & lanemask_lt())] =
+              make_int2(recs[c], keys[c] - R0 - 32 * s2);
+        run[s2] += __popcll(m[c][s2]);
+      }
     }
   };
-  int2 fe = load_fe(t0);
-  for (int64_t tb = t0; tb < t1; tb += 64) {
-    const int n = fe.y - fe.x;
-    int incl = n;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
+  // this wave's block from the four queues of a round, in record order
+  auto consume = [&](int buf) {
+    int seg[kRowWaves + 1], off[kRowWaves];
+    seg[0] = 0;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      off[w] = __builtin_amdgcn_readfirstlane(qoff[buf][w][wv]);
+      seg[w + 1] = seg[w] + __builtin_amdgcn_readfirstlane(qcnt[buf][w][wv]);
     }
-    const int T = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
-    const int64_t t = tb + lane;
-    wave_lds_sync();  // the previous batch's searches are done
-    ex_s[lane] = incl - n;
-    base_s[lane] = t < t1 ? int((b * P.S_q + t) * P.rec_stride) + fe.x : 0;
-    wave_lds_sync();
-    fe = load_fe(tb + 64);  // the next batch's runs
-    for (int p0 = 0; p0 < T; p0 += 64 * kPiece) {
-      // the keys of kPiece x 64 records, their reads in flight together
-      int recs[kPiece], keys[kPiece];
+    const int n = seg[kRowWaves];
+    if (n == 0) return;
+    // entry j of the block's sequence ({0, -1} past the end: record 0, no key)
+    auto entry = [&](int j) -> int2 {
+      int w = 0;
 #pragma unroll
-      for (int c = 0; c < kPiece; ++c) keys[c] = locate(p0 + 64 * c + lane, T, recs[c]);
-      // the records of the wave's keys, in record order, into the queue
-      int qn = 0;
+      for (int w2 = 1; w2 < kRowWaves; ++w2) w += j >= seg[w2] ? 1 : 0;
+      int o2 = 0, s0 = 0;
 #pragma unroll
-      for (int c = 0; c < kPiece; ++c) {
-        const int loc = keys[c] - k0;
-        const bool sel = unsigned(loc) < unsigned(KW);
-        const uint64_t m = ballot(sel);
-        if (sel) queue[qn + __popcll(m & lanemask_lt())] = make_int2(recs[c], loc);
-        qn += __popcll(m);
+      for (int w2 = 0; w2 < kRowWaves; ++w2)
+        if (w2 == w) o2 = off[w2], s0 = seg[w2];
+      return j < n ? queue[buf][w][o2 + j - s0] : make_int2(0, -1);
+    };
+    // batch bi's rows into stage bi % kStages: copy i, lane L fills 16-byte
+    // slot 64i + L (row r = slot / CPR, stored chunk slot % CPR)
+    auto issue = [&](int bi) {
+      const uint32_t dst = stage0 + uint32_t((bi % kStages) * 16 * RP);
+#pragma unroll
+      for (int i = 0; i < kDmaB; ++i) {
+        const int slot = 64 * i + lane;
+        const int r = slot / CPR;
+        const int c = (slot % CPR) ^ (((r / RPB) & 3) * (CPR / 4));
+        const int rec = entry(16 * bi + r).x;
+        dma16(dst + uint32_t(1024 * i), P.crow, uint32_t(rec) * uint32_t(RP) + uint32_t(16 * c));
+      }
+    };
+    const int nbat = (n + 15) / 16;
+    // every copy is issued (batches past the end copy record 0 and add
+    // nothing), so the wait before each batch counts exactly the two newer ones
+    issue(0);
+    issue(1);
+    for (int bi = 0; bi < nbat; ++bi) {
+      issue(bi + 2);
+      const int2 eu = entry(16 * bi + (lane & 15));  // lane u < 16: entry u of the batch
+      if (lane < 16 && eu.y >= 0) onehot_s[wv][eu.y * 16 + lane] = 0x3f80;  // bf16 1.0
+      wave_lds_sync();
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&onehot_s[wv][l32 * 16 + 8 * half]);
+      wait_vm<2 * kDmaB>();  // this batch's rows are in LDS
+      const unsigned char* st = &stage_s[wv][bi % kStages][0];
+#pragma unroll
+      for (int nb = 0; nb < ND; ++nb) {
+        const int col0 = 32 * nb + 16 * ((lane >> 4) & 1);
+        u32x4_t bv;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int s16 = lane & 15;
+          const unsigned char* ad = st + st_at(8 * half + 4 * h + (s16 >> 2), (col0 + 4 * (s16 & 3)) * 2);
+          const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                        (__attribute__((address_space(3))) i16x4_t*)(ad)));
+          bv[2 * h] = v.x;
+          bv[2 * h + 1] = v.y;
+        }
+        acc[nb] = mfma32(a, bv, acc[nb]);
       }
       wave_lds_sync();
-      if (qn > 0) {
-        // rows kBatch at a time; the next kBatch are read while the current
-        // ones are added.  Every read is issued (entries past the queue read
-        // record 0 and add nothing), so the compiler's wait before each add
-        // covers only the reads issued before it.
-        uint32_t va[kBatch], vb[kBatch];
-        int la[kBatch], lb[kBatch];
-        auto fetch = [&](int q0, uint32_t(&v)[kBatch], int(&l)[kBatch]) {
-          const int qi = q0 + (lane & (kBatch - 1));
-          const int2 e = qi < qn ? queue[qi] : make_int2(0, -1);
-#pragma unroll
-          for (int u = 0; u < kBatch; ++u) {
-            l[u] = __builtin_amdgcn_readlane(e.y, u);
-            v[u] = row_at(__builtin_amdgcn_readlane(e.x, u));
-          }
-        };
-        fetch(0, va, la);
-        for (int q0 = 0; q0 < qn; q0 += 2 * kBatch) {
-          fetch(q0 + kBatch, vb, lb);
-#pragma unroll
-          for (int u = 0; u < kBatch; ++u) add_row(la[u], va[u]);
-          fetch(q0 + 2 * kBatch, va, la);
-#pragma unroll
-          for (int u = 0; u < kBatch; ++u) add_row(lb[u], vb[u]);
-        }
-      }
-      wave_lds_sync();  // the queue is read before the next piece fills it
+      if (lane < 16 && eu.y >= 0) onehot_s[wv][eu.y * 16 + lane] = 0;
     }
+    wait_vm<0>();  // the copies past the end have landed before their stages are reused
+  };
+
+  const int rounds = (T + kRound - 1) / kRound;
+  if (rounds > 0) {
+    scan_issue(0);
+    scan_queue(0);
   }
-  float* dst = P.slab + ((b * P.NQB + qb) * (P.NR * kRangeKeys) + k0) * D;
-  if (lane < NL) {
+  __syncthreads();
+  for (int i = 0; i < rounds; ++i) {
+    // keys in flight while this round's rows are added (issued unconditionally:
+    // past the last round no record is found and nothing is read, and the
+    // compiler's waits in consume stay exact)
+    scan_issue(i + 1);
+    consume(i & 1);
+    if (i + 1 < rounds) scan_queue((i + 1) & 1);
+    __syncthreads();  // round i's queues read by every wave; round i+1's written
+  }
+
+  float* dst = P.slab + ((b * P.NQB + qb) * (P.NR * kRangeKeys) + R0 + 32 * wv) * D;
 #pragma unroll
-    for (int k = 0; k < KW; ++k) {
-      if (k0 + k < P.S_k) {
-        if (E == 2)
-          *reinterpret_cast<float2*>(dst + k * D + 2 * lane) = make_float2(acc0[k], acc1[k]);
-        else
-          dst[k * D + lane] = acc0[k];
+  for (int nb = 0; nb < ND; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int k = 8 * i + 4 * half + rr;
+        if (R0 + 32 * wv + k < P.S_k) dst[k * D + 32 * nb + l32] = acc[nb][4 * i + rr];
       }
-    }
-  }
 }
 
 hipError_t launch_sum(const Problem& P, hipStream_t stream) {
@@ -733,8 +845,8 @@ hipError_t launch_sum(const Problem& P, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_rows_t(const Problem& P, hipStream_t stream) {
-  const dim3 grid(unsigned(P.NR * kRowBlocks), unsigned(P.NQB), unsigned(P.B));
-  dk_rows_kernel<D><<<grid, 64, 0, stream>>>(P);
+  const dim3 grid(unsigned(P.NR), unsigned(P.NQB), unsigned(P.B));
+  dk_rows_kernel<D><<<grid, 64 * kRowWaves, 0, stream>>>(P);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   stage_done(2, "dk_rows_kernel");

@@ -544,7 +544,8 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int ch = lane % SCPR;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + stg_at(row, ch));
         const int pos = reinterpret_cast<const int*>(st + kSlots * 8)[row];
-        *reinterpret_cast<u32x4_t*>(P.crow + rec_of(pos) * D + 32 * mlo + 8 * ch) = v;
+        // read once, by the next kernel: streamed past the caches
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(P.crow + rec_of(pos) * D + 32 * mlo + 8 * ch));
       }
       wave_lds_sync();  // staging read before the wave's K rows take its place
     }
@@ -661,7 +662,9 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // ---- row epilogue: dQ = w * dQ', dW -----------------------------------------
   // dQ' register 4*i + rr of lane (half) is GEMM2's row m = 8*i + 4*half + rr,
-  // i.e. head 32*g + rotl5(m).  bf16 outputs round the same fp32 values.
+  // i.e. head 32*g + rotl5(m).  bf16 outputs round the same fp32 values.  No
+  // later kernel of the call reads dQ: its stores are non-temporal, so that
+  // its lines do not sit dirty in the caches that the next kernels read through.
   const float tot = dw_acc + __shfl_xor(dw_acc, 32, 64);
   auto epilogue = [&](auto* dq, auto* dw, auto cvt) {
     auto* dqrow = dq + r * P.H * D;
@@ -675,7 +678,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
         if (h < H) {
 #pragma unroll
           for (int nd = 0; nd < ND; ++nd)
-            dqrow[h * D + l32 + 32 * nd] = cvt(wh * dqacc[nd][4 * i + rr]);
+            __builtin_nontemporal_store(cvt(wh * dqacc[nd][4 * i + rr]), &dqrow[h * D + l32 + 32 * nd]);
         }
       }
     }

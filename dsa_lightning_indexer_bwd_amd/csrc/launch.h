@@ -26,9 +26,14 @@ enum DkRoute : int {
 // query's (w*q)^T into the range's workgroup: its cost follows (queries x
 // ranges).  Per-slot dK rows cost one fp32 row of D per selected slot, written
 // and read once: they win when a row selects few keys per range.
-// force: 0 = by density, 1 = key ranges, 2 = slot rows.
-inline bool use_slot_rows(int64_t S_k, int64_t row_len, bool dense, int force) {
-  if (dense) return false;
+// The slot-row sum copies rows with 32-bit byte offsets, so the route needs
+// all rows in 4 GiB.  force: 0 = by density, 1 = key ranges, 2 = slot rows.
+inline bool slot_rows_fit(int64_t B, int64_t S_q, int64_t D, int64_t row_len) {
+  return (B * S_q * row_len + 1) * D * 2 < (int64_t(1) << 32);
+}
+inline bool use_slot_rows(int64_t B, int64_t S_q, int64_t S_k, int64_t D, int64_t row_len, bool dense,
+                          int force) {
+  if (dense || !slot_rows_fit(B, S_q, D, row_len)) return false;
   if (force) return force == 2;
   return row_len * 16 <= S_k;
 }

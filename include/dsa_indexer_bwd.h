@@ -100,7 +100,9 @@ extern "C" {
                                        density (by default a sparse call with topk*16 > S_k) */
 #define IBWD_FLAG_DK_SLOT_ROWS 32u  /* indexer_bwd_sparse only: deterministic dK from per-slot
                                        rows at any density (by default when topk*16 <= S_k);
-                                       excludes IBWD_FLAG_DK_KEY_RANGES */
+                                       needs (B*S_q*topk + 1)*D*2 < 2^32 (the default falls
+                                       back to key ranges beyond); excludes
+                                       IBWD_FLAG_DK_KEY_RANGES */
 
 /*
  * indexer_bwd_sparse — backward of the top-k (sparse) indexer.

@@ -76,6 +76,12 @@ def test_dk_route_flags_and_workspace():
         slot_rows_bytes = (rows * topk * (8 + 4) + (rows * topk + 1) * 128 * 2 + rows * NR * 8
                            + NQB * NR * 128 * 128 * 4)
         assert slot_rows_bytes <= sr <= slot_rows_bytes + 5 * 256
+    # rows past 4 GiB: the density rule falls back to key ranges, the forced route is refused
+    big = (1, 8192, 1 << 18, 64, 128, 2048)      # 8192*2048 slots of 256-byte rows = 4 GiB
+    assert wsb(False, *big, SR) == 0
+    assert wsb(False, *big, 0) == wsb(False, *big, KR) > 0
+    assert call_sparse(sparse_args(S_q=8192, S_k=1 << 18, H=64, D=128, topk=2048, flags=SR,
+                                   ws_bytes=1 << 40)) == ibwd.IBWD_ERR_INVALID_ARGUMENT
     # the dense call always takes the key ranges: the slot-row flag is an error there
     assert wsb(True, 1, 64, 64, 4, 32, 0, SR) == 0
     assert wsb(True, 1, 64, 64, 4, 32, 0, KR) == wsb(True, 1, 64, 64, 4, 32, 0, 0)
