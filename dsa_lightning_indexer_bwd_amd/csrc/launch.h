@@ -35,7 +35,7 @@ inline bool use_slot_rows(int64_t B, int64_t S_q, int64_t S_k, int64_t D, int64_
                           int force) {
   if (dense || !slot_rows_fit(B, S_q, D, row_len)) return false;
   if (force) return force == 2;
-  return row_len * 16 <= S_k;
+  return row_len * 8 <= S_k;
 }
 
 // Workspace layout of the two-pass dK route.  A row's valid slots are stored

@@ -97,9 +97,9 @@ extern "C" {
                                       error of note.  Default route only; not with
                                       IBWD_FLAG_ATOMIC_DK, whose dK accumulates in d_k */
 #define IBWD_FLAG_DK_KEY_RANGES 16u /* deterministic dK by the key-range GEMM at any selection
-                                       density (by default a sparse call with topk*16 > S_k) */
+                                       density (by default a sparse call with topk*8 > S_k) */
 #define IBWD_FLAG_DK_SLOT_ROWS 32u  /* indexer_bwd_sparse only: deterministic dK from per-slot
-                                       rows at any density (by default when topk*16 <= S_k);
+                                       rows at any density (by default when topk*8 <= S_k);
                                        needs (B*S_q*topk + 1)*D*2 < 2^32 (the default falls
                                        back to key ranges beyond); excludes
                                        IBWD_FLAG_DK_KEY_RANGES */

@@ -61,11 +61,11 @@ def test_strerror_and_workspace():
 
 def test_dk_route_flags_and_workspace():
     """The deterministic dK route follows the selection density (slot rows when
-    topk*16 <= S_k) unless a flag forces one; the workspace follows the route."""
+    topk*8 <= S_k) unless a flag forces one; the workspace follows the route."""
     KR, SR = ibwd.IBWD_FLAG_DK_KEY_RANGES, ibwd.IBWD_FLAG_DK_SLOT_ROWS
     wsb = ibwd.indexer_bwd_workspace_bytes
     rows, NR, NQB = 8192, 32, 16
-    for topk, auto_rows in ((128, True), (256, True), (257, False), (1024, False)):
+    for topk, auto_rows in ((128, True), (512, True), (513, False), (1024, False)):
         auto = wsb(False, 1, 8192, 4096, 64, 128, topk, 0)
         kr = wsb(False, 1, 8192, 4096, 64, 128, topk, KR)
         sr = wsb(False, 1, 8192, 4096, 64, 128, topk, SR)

@@ -415,13 +415,16 @@ def test_invalid_call_leaves_outputs_untouched(ibwd):
 # of d_q, d_w and d_k against the full oracle backward (seconds on the host
 # cores)
 
-@pytest.mark.parametrize("name", ["sparse", "anchor", "wide", "dense", "anchor-topk128"])
+@pytest.mark.parametrize("name", ["sparse", "anchor", "wide", "dense", "anchor-topk128", "sparse-key-ranges"])
 def test_full_size_workload(ibwd, name):
-    """The four workloads, and the anchor at topk 128 (the slot-row dK route)."""
+    """The four workloads (sparse, at 512 of 4096 keys, on the slot-row dK route
+    by density), the anchor at topk 128, and the sparse workload on the key-range
+    route."""
     log(f"case: full-size {name}")
-    wl = dataclasses.replace(WORKLOADS["anchor"], topk=128) if name == "anchor-topk128" else name
+    wl = dataclasses.replace(WORKLOADS["anchor"], topk=128) if name == "anchor-topk128" else \
+        "sparse" if name == "sparse-key-ranges" else name
     x = make_inputs(wl, device="cuda:0")
-    got = run(ibwd, x)
+    got = run(ibwd, x, dk_route="key_ranges" if name == "sparse-key-ranges" else "auto")
     ref = oracle.Problem.from_inputs(x).backward()
     assert_parity(f"full-{name}", got, ref)
     # Euler identity of the 1-homogeneous score at every (t,h): <q, dQ> = w dW
@@ -472,7 +475,7 @@ def test_stage_hook_reports_every_kernel(ibwd):
     seen = []
     ibwd.set_stage_hook(lambda stage, name: seen.append((stage, name)))
     try:
-        a = run(ibwd, x)
+        a = run(ibwd, x, dk_route="key_ranges")
         b = run(ibwd, x, atomic_dk=True)
         run(ibwd, y)  # 128 of 4096 keys: the slot-row route by density
     finally:
@@ -481,7 +484,7 @@ def test_stage_hook_reports_every_kernel(ibwd):
                     (3, "dk_sum_kernel"), (0, "zero_u32_kernel"), (1, "row_kernel"),
                     (0, "row_prep_kernel"), (1, "row_export_kernel"), (2, "dk_rows_kernel"),
                     (3, "dk_sum_kernel")]
-    c = run(ibwd, x)  # hook removed: nothing more is reported
+    c = run(ibwd, x, dk_route="key_ranges")  # hook removed: nothing more is reported
     assert len(seen) == 10
     assert all(np.array_equal(u, v) for u, v in zip(a, c))
     assert_parity("hook-atomic", b, oracle.Problem.from_inputs(x).backward())
