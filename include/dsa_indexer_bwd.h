@@ -57,6 +57,16 @@
  *     cores (dI enters that GEMM rounded to bf16, like w*q), then the per
  *     query-block partial sums are added in a fixed order.  d_q, d_w and d_k
  *     are all bitwise reproducible run to run.
+ *     When a row selects few keys per 128-key range (topk*8 <= S_k by
+ *     default; IBWD_FLAG_DK_SLOT_ROWS / IBWD_FLAG_DK_KEY_RANGES force either
+ *     way) the deterministic call takes the slot-row route instead: the row
+ *     kernel computes each valid slot's dK row dI * sum_h [S > 0] (w*q)[h,:]
+ *     (PR #730 harness `ref_grads`, the `contrib` rows before `index_add_`)
+ *     on the matrix cores, rounds it to bf16 and stores it with the slot's key,
+ *     and a second kernel adds the rows of each key in a fixed order.  d_q and
+ *     d_w are the same bits on both routes; d_k differs by the rounding of the
+ *     rows (relRMS about 3e-3 against the fp64 reference, 2e-3 on the key
+ *     ranges) and is again bitwise reproducible.
  *     IBWD_FLAG_ATOMIC_DK selects the single-pass route of the pages' design
  *     instead: fp32 global atomics straight from the row kernel, no workspace,
  *     and d_k may then differ in the last bits between runs (PR #549: dK uses
@@ -185,13 +195,16 @@ int indexer_bwd_dense(const void* q, const void* k, const float* w, const float*
 /*
  * indexer_bwd_workspace_bytes — device scratch needed by a call with these
  * arguments (dense != 0 selects indexer_bwd_dense; topk is ignored then).
- * The default route needs 16 bytes per record entry (topk + 3 per 128-key
+ * The key-range route needs 16 bytes per record entry (topk + 3 per 128-key
  * range per row, for aligning the ranges), 8 bytes per slot for each slot's
  * record position and dI, 8 bytes per row and key range for the range table,
  * (w*q)^T in bf16 (2*H_pad*D bytes per row, H_pad = 32 or 64) and the per
  * query-block dK partial sums (about 385 MB in all at B=1, S_q=8192, S_k=4096,
- * H=64, D=128, topk=1024; about 990 MB for the dense variant at that shape);
- * IBWD_FLAG_ATOMIC_DK needs none (0).
+ * H=64, D=128, topk=1024; about 511 MB for the dense variant at that shape).
+ * The slot-row route needs 8 + 4 + 2*D bytes per slot (position and dI, key,
+ * bf16 dK row), one spare row, the range table and the partial sums (about
+ * 317 MB at topk=128 of the same shape).  The flags choose the route, so pass
+ * the call's flags.  IBWD_FLAG_ATOMIC_DK needs none (0).
  * Returns 0 for invalid shapes as well; the call itself reports those.
  */
 size_t indexer_bwd_workspace_bytes(int dense, int64_t B, int64_t S_q, int64_t S_k, int64_t H,
