@@ -663,10 +663,8 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
   // ---- row epilogue: dQ = w * dQ', dW -----------------------------------------
   // dQ' register 4*i + rr of lane (half) is GEMM2's row m = 8*i + 4*half + rr,
   // i.e. head 32*g + rotl5(m).  bf16 outputs round the same fp32 values.  No
-  // later kernel of the call reads dQ: fp32 stores (128 bytes per half-wave,
-  // whole cache lines) are non-temporal, so that its lines do not sit dirty in
-  // the caches that the next kernels read through; bf16 stores (half lines)
-  // stay ordinary, since non-temporal partial lines cost more than they save.
+  // later kernel of the call reads dQ: its stores are non-temporal, so that
+  // its lines do not sit dirty in the caches that the next kernels read through.
   const float tot = dw_acc + __shfl_xor(dw_acc, 32, 64);
   auto epilogue = [&](auto* dq, auto* dw, auto cvt) {
     auto* dqrow = dq + r * P.H * D;
@@ -680,10 +678,7 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
         if (h < H) {
 #pragma unroll
           for (int nd = 0; nd < ND; ++nd)
-            if (P.bf16_out)
-              dqrow[h * D + l32 + 32 * nd] = cvt(wh * dqacc[nd][4 * i + rr]);
-            else
-              __builtin_nontemporal_store(cvt(wh * dqacc[nd][4 * i + rr]), &dqrow[h * D + l32 + 32 * nd]);
+            __builtin_nontemporal_store(cvt(wh * dqacc[nd][4 * i + rr]), &dqrow[h * D + l32 + 32 * nd]);
         }
       }
     }
