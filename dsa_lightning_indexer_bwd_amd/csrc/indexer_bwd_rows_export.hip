@@ -538,7 +538,10 @@ __global__ __launch_bounds__(64 * NG) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (D >= 64) {
       wave_lds_sync();
       constexpr int kRowsPer = 64 / SCPR;  // staged rows per 16-byte-lane pass
-#pragma unroll
+      // fully unrolled, except for one wave at D = 128 (eight passes), where
+      // hoisting every read would spill
+      constexpr int kUnroll = kSlots / kRowsPer > 4 ? 2 : kSlots / kRowsPer;
+#pragma unroll kUnroll
       for (int it = 0; it < kSlots / kRowsPer; ++it) {
         const int row = it * kRowsPer + lane / SCPR;
         const int ch = lane % SCPR;

@@ -119,7 +119,8 @@ ROUTES = ["key_ranges", "slot_rows"]
 
 @pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("topk,H,D,pad", [(1, 4, 32, 0.0), (37, 64, 128, 0.1), (100, 33, 64, 0.3),
-                                          (129, 1, 32, 0.05), (300, 64, 64, 0.5), (16, 17, 128, 1.0)])
+                                          (129, 1, 32, 0.05), (300, 64, 64, 0.5), (16, 17, 128, 1.0),
+                                          (70, 32, 128, 0.2)])
 def test_ragged_and_odd_shapes(ibwd, topk, H, D, pad, route):
     """topk not a multiple of any chunk, H below/above MFMA tiles, every D, heavy
     padding, an all-padding workload; both deterministic dK routes."""
