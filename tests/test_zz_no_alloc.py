@@ -1,12 +1,15 @@
 """The allocation-free entry point (indexer_bwd_sparse_noalloc) against
 indexer_bwd_sparse: two calls in a row on the library's scratch array, the
 second smaller, each bitwise equal to the workspace call (same kernels, same
-deterministic route); a call too large for the array is rejected before
+deterministic route, the key-range route at topk 1024 and the slot-row route
+at topk 128 of 4096 keys); a call too large for the array is rejected before
 anything is written."""
+import dataclasses
+
 import numpy as np
 import pytest
 
-from synth import make_inputs
+from synth import WORKLOADS, make_inputs
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -45,12 +48,16 @@ def _host(r):
             for a in r]
 
 
+@pytest.mark.parametrize("topk", [1024, 128])
 @pytest.mark.parametrize("bf16_out", [False, True])
-def test_noalloc_matches_workspace_call_twice(ibwd, bf16_out):
-    print(f"case: noalloc bf16_out={bf16_out}", flush=True)
+def test_noalloc_matches_workspace_call_twice(ibwd, bf16_out, topk):
+    print(f"case: noalloc bf16_out={bf16_out} topk={topk}", flush=True)
     dt = torch.bfloat16 if bf16_out else torch.float32
+    wl = dataclasses.replace(WORKLOADS["anchor"], topk=topk)
+    assert ibwd.indexer_bwd_workspace_bytes(False, 1, 2048, 4096, 64, 128, topk, 0) <= \
+        ibwd.IBWD_NOALLOC_SCRATCH_BYTES
     for S_q, seed, sm, gl in ((2048, 81, 1.0, 1.0), (300, 82, 0.7, 1.3)):
-        x = make_inputs("anchor", S_q=S_q, seed=seed)
+        x = make_inputs(wl, S_q=S_q, seed=seed)
         t = _dev(x)
         want = ibwd.indexer_bwd_sparse(t["q"], t["k"], t["w"], t["ids"], t["I"], t["p"],
                                        sm_scale=sm, grad_loss=gl, bf16_out=bf16_out)
