@@ -609,7 +609,8 @@ template <int D>
 __global__ __launch_bounds__(64 * kRowWaves) void dk_rows_kernel(Problem P) {
   constexpr int kScan = 4;             // 64-record chunks a wave scans per round
   constexpr int kRound = 64 * kScan * kRowWaves;
-  __shared__ int ex_s[kMaxQueryBlock + 1];  // start of each query's run in the sequence
+  static_assert(2 * 64 * kRowWaves >= kMaxQueryBlock, "two queries per thread cover a query block");
+  __shared__ int ex_s[kMaxQueryBlock];      // start of each query's run in the sequence
   __shared__ int base_s[kMaxQueryBlock];    // record index of each run's first record
   __shared__ int2 queue[2][kRowWaves][64 * kScan];  // {record, key - 32s}, by block, in order
   __shared__ int qoff[2][kRowWaves][kRowWaves];      // [buf][scanning wave][block] start
