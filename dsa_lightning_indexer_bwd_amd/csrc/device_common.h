@@ -170,5 +170,9 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   const int l = threadIdx.x & 63;
   return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
+// Set bits of m at lanes below this one (v_mbcnt; m may differ per lane).
+__device__ __forceinline__ int bits_below(uint64_t m) {
+  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+}
 
 }  // namespace ibwd

@@ -730,7 +730,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void dk_rows_kernel(Problem P) {
 #pragma unroll
       for (int s2 = 0; s2 < kRowWaves; ++s2) {
         if (blk == s2)
-          queue[buf][wv][run[s2] + __popcll(m[c][s2] & lanemask_lt())] =
+          queue[buf][wv][run[s2] + bits_below(m[c][s2])] =
               make_int2(recs[c], keys[c] - R0 - 32 * s2);
         run[s2] += __popcll(m[c][s2]);
       }

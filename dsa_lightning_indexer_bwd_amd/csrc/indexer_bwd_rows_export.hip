@@ -131,14 +131,19 @@ struct Raw {
 __device__ __forceinline__ int rotl5(int b) { return ((b << 1) | (b >> 4)) & 31; }
 
 // Lanes of the wave whose range equals this lane's (valid lanes only), from
-// nbits ballots of the range bits.
+// nbits ballots of the range bits: each lane keeps the ballot of bit b where
+// its own bit b is set and the complement where it is clear (an XNOR with the
+// bit spread over a word).
 __device__ __forceinline__ uint64_t same_range_lanes(bool valid, int r, int nbits) {
-  uint64_t same = ballot(valid);
+  const uint64_t vm = ballot(valid);
+  uint32_t lo = uint32_t(vm), hi = uint32_t(vm >> 32);
   for (int b = 0; b < nbits; ++b) {
-    const uint64_t bb = ballot(valid && ((r >> b) & 1));
-    same &= ((r >> b) & 1) ? bb : ~bb;
+    const uint32_t x = uint32_t(int(uint32_t(r) << (31 - b)) >> 31);  // all ones where bit b of r is set
+    const uint64_t bb = ballot(x != 0u) & vm;
+    lo &= ~(uint32_t(bb) ^ x);
+    hi &= ~(uint32_t(bb >> 32) ^ x);
   }
-  return same;
+  return uint64_t(hi) << 32 | lo;
 }
 
 // Per query row, before the row kernel: the softmax statistics over the valid
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
           const bool valid = key >= 0;
           const int rg = valid ? key / RK : 0;
           const uint64_t same = same_range_lanes(valid, rg, nbits);
-          if (valid && (same & lanemask_lt()) == 0) cursor[rg] += __popcll(same);
+          if (valid && bits_below(same) == 0) cursor[rg] += __popcll(same);
           lds_order();
         }
       });
@@ -254,9 +259,10 @@ __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
           const int rg = valid ? key / RK : 0;
           const uint64_t same = same_range_lanes(valid, rg, nbits);
           const int base = valid ? cursor[rg] : 0;
-          pos = base + __popcll(same & lanemask_lt());
+          const int below = bits_below(same);
+          pos = base + below;
           lds_order();
-          if (valid && (same & lanemask_lt()) == 0) cursor[rg] = base + __popcll(same);
+          if (valid && below == 0) cursor[rg] = base + __popcll(same);
           lds_order();
         }
         const float dI = valid ? slot_dI(iv[u], pv[u], c2, st.x, st.y, coef) : 0.f;

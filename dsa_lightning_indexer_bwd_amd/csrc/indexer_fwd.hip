@@ -344,8 +344,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkProblem P) {
         etot += int(part[1][w]);
       }
       __syncthreads();
-      gb += __popcll(mg & lanemask_lt());
-      eb += __popcll(me & lanemask_lt());
+      gb += bits_below(mg);
+      eb += bits_below(me);
       if (gt || (eq && eb < keq)) {
         const int pos = gb + (eb < keq ? eb : keq);
         ids[pos] = s;
