@@ -122,17 +122,18 @@ __device__ __forceinline__ int local_key(int id, int base, int S_k) {
 // keeps a running max and a sum rescaled to it, then the wave combines them.
 // c2*I is rounded before any max is subtracted (no contraction into a
 // multiply-add), so the largest logit contributes 2^0 = 1 exactly.
-// on_group(j, key) is called by every lane, in uniform control flow, once per
-// slot position j = j0 + 64u + lane (key < 0 for padding and positions past n).
+// on_group(g, j, key) is called by every lane, in uniform control flow, once per
+// slot position j = 64g + lane (key < 0 for padding and positions past n).  With
+// MAXN > 0 (rows of at most MAXN slots) the loop is unrolled and g is a constant.
 // Both row kernels use this and slot_dI, so their dI agree bit for bit.
-template <typename IdAt, typename KeyOf, typename OnGroup>
+template <int MAXN = 0, typename IdAt, typename KeyOf, typename OnGroup>
 __device__ __forceinline__ float2 row_softmax_stats(int n, const float* __restrict__ Irow, float c2,
                                                     IdAt id_at, KeyOf key_of, OnGroup on_group) {
 #pragma clang fp contract(off)
   constexpr int kU = 8;  // loads in flight per lane
   const int lane = threadIdx.x & 63;
   float m2 = -INFINITY, z = 0.f;
-  for (int j0 = 0; j0 < n; j0 += 64 * kU) {
+  auto batch = [&](int j0) {
     int idv[kU];
     float iv[kU];
 #pragma unroll
@@ -151,8 +152,16 @@ __device__ __forceinline__ float2 row_softmax_stats(int n, const float* __restri
         z = z * __builtin_amdgcn_exp2f(m2 - mn) + __builtin_amdgcn_exp2f(v - mn);
         m2 = mn;
       }
-      if (j0 + 64 * u < n) on_group(j0 + 64 * u + lane, key);
+      if (j0 + 64 * u < n) on_group((j0 >> 6) + u, j0 + 64 * u + lane, key);
     }
+  };
+  if constexpr (MAXN > 0) {
+    // n <= MAXN: unrolled, so that on_group's group index is a constant
+#pragma unroll
+    for (int j0 = 0; j0 < MAXN; j0 += 64 * kU)
+      if (j0 < n) batch(j0);
+  } else {
+    for (int j0 = 0; j0 < n; j0 += 64 * kU) batch(j0);
   }
   const float mw = wave_max(m2);
   z = m2 > -INFINITY ? z * __builtin_amdgcn_exp2f(m2 - mw) : 0.f;

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64, 1) void row_kernel(Problem P) {
   // ---- softmax statistics over the valid slots ---------------------------------
   const float c2 = P.sm_scale * 1.4426950408889634f;  // base-2 logit scale
   const float2 st = row_softmax_stats(
-      n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [](int, int) {});
+      n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [](int, int, int) {});
   const float m2 = st.x, invZ = st.y;
   const float coef = P.grad_loss * P.sm_scale;
 

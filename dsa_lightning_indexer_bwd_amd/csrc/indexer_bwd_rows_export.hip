@@ -130,6 +130,8 @@ struct Raw {
 
 __device__ __forceinline__ int rotl5(int b) { return ((b << 1) | (b >> 4)) & 31; }
 
+constexpr int kPrepGroups = 16;  // 64-slot groups whose range masks the prep kernel keeps
+
 // Lanes of the wave whose range equals this lane's (valid lanes only), from
 // nbits ballots of the range bits: each lane keeps the ballot of bit b where
 // its own bit b is set and the complement where it is clear (an XNOR with the
@@ -159,7 +161,9 @@ __device__ __forceinline__ uint64_t same_range_lanes(bool valid, int r, int nbit
 //   pass 2: positions (range start + earlier slots of the range, from the
 //           same ballots) and dI, as {position or -1, dI} per slot
 // PACKED (slot-row route): ranges follow each other without alignment.
-template <bool DENSE, bool PACKED>
+// MAXG > 0: rows of at most 64*MAXG slots; pass 1's range masks stay in
+// registers for pass 2, which then matches no ranges itself.
+template <bool DENSE, bool PACKED, int MAXG>
 __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
   extern __shared__ int cursor[];  // one int per key range
   const int lane = threadIdx.x;
@@ -195,12 +199,14 @@ __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
     for (int i = lane; i < NR; i += 64) cursor[i] = 0;
     lds_order();
   }
-  const float2 st = row_softmax_stats(
-      n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [&](int, int key) {
+  uint64_t sm[MAXG > 0 ? MAXG : 1];  // pass 1's range mask of each 64-slot group
+  const float2 st = row_softmax_stats<64 * MAXG>(
+      n, Irow, c2, [&](int j) { return DENSE ? 0 : idrow[j]; }, key_of, [&](int g, int, int key) {
         if (!DENSE) {
           const bool valid = key >= 0;
           const int rg = valid ? key / RK : 0;
           const uint64_t same = same_range_lanes(valid, rg, nbits);
+          if (MAXG > 0) sm[g] = same;
           if (valid && bits_below(same) == 0) cursor[rg] += __popcll(same);
           lds_order();
         }
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
 
   // ---- pass 2: record position and dI of every slot ------------------------------
   constexpr int kU = 4;  // loads in flight per lane and array
-  for (int j0 = 0; j0 < n; j0 += 64 * kU) {
+  auto batch = [&](int j0) {
     int idv[kU];
     float iv[kU], pv[kU];
 #pragma unroll
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
         int pos = j;
         if (!DENSE) {
           const int rg = valid ? key / RK : 0;
-          const uint64_t same = same_range_lanes(valid, rg, nbits);
+          const uint64_t same = MAXG > 0 ? sm[(j0 >> 6) + u] : same_range_lanes(valid, rg, nbits);
           const int base = valid ? cursor[rg] : 0;
           const int below = bits_below(same);
           pos = base + below;
@@ -269,6 +275,13 @@ __global__ __launch_bounds__(64) void row_prep_kernel(Problem P) {
         if (j < n) slot[j] = make_int2(valid ? pos : -1, __float_as_int(dI));
       }
     }
+  };
+  if constexpr (MAXG > 0) {
+#pragma unroll
+    for (int j0 = 0; j0 < 64 * MAXG; j0 += 64 * kU)
+      if (j0 < n) batch(j0);
+  } else {
+    for (int j0 = 0; j0 < n; j0 += 64 * kU) batch(j0);
   }
 }
 
@@ -715,7 +728,11 @@ void launch_export(const Problem& P, hipStream_t stream) {
 template <int D, bool DENSE, bool CROWS>
 hipError_t launch_t(const Problem& P, hipStream_t stream) {
   const dim3 grid(unsigned(P.B * P.S_q));
-  row_prep_kernel<DENSE, CROWS><<<grid, 64, size_t(P.NR) * 4, stream>>>(P);
+  // rows of up to 1024 slots keep pass 1's range masks in registers
+  if (!DENSE && P.row_len <= 64 * kPrepGroups)
+    row_prep_kernel<DENSE, CROWS, kPrepGroups><<<grid, 64, size_t(P.NR) * 4, stream>>>(P);
+  else
+    row_prep_kernel<DENSE, CROWS, 0><<<grid, 64, size_t(P.NR) * 4, stream>>>(P);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   stage_done(0, "row_prep_kernel");
