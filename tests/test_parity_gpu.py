@@ -120,10 +120,13 @@ ROUTES = ["key_ranges", "slot_rows"]
 @pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("topk,H,D,pad", [(1, 4, 32, 0.0), (37, 64, 128, 0.1), (100, 33, 64, 0.3),
                                           (129, 1, 32, 0.05), (300, 64, 64, 0.5), (16, 17, 128, 1.0),
-                                          (70, 32, 128, 0.2)])
+                                          (70, 32, 128, 0.2), (1000, 8, 32, 0.2), (1024, 64, 128, 0.1),
+                                          (1025, 64, 64, 0.1)])
 def test_ragged_and_odd_shapes(ibwd, topk, H, D, pad, route):
     """topk not a multiple of any chunk, H below/above MFMA tiles, every D, heavy
-    padding, an all-padding workload; both deterministic dK routes."""
+    padding, an all-padding workload; both deterministic dK routes.  1000, 1024
+    and 1025 sit at the prep kernel's limit for keeping its range masks in
+    registers (rows of at most 1024 slots; longer rows take the other build)."""
     log(f"case: ragged topk={topk} H={H} D={D} pad={pad} route={route}")
     wl = dataclasses.replace(WORKLOADS["tiny"], H=H, D=D, S_q=48, S_k=max(160, topk + 1), topk=topk,
                              pad_frac=pad)
